@@ -1,0 +1,290 @@
+"""Pins for the CPU oracle: each check ties it to something other than itself.
+
+The pins are closed forms (row sums, a single visible key, identical keys,
+shift invariance), a library routine (torch's CPU scaled_dot_product_attention
+in float64), bit-exact identities (gather through a permuted block table,
+causality), and numbers printed on the pages (tests/golden/). Each is chosen so
+that a plausible slip in the oracle (a dropped scale, a wrong sign, a wrong
+head order, a transposed operand, an off-by-one in the mask or the slot map)
+fails at least one of them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import attention_oracle as ao
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rnd(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def torch_sdpa(q, k, v, scale, causal, gqa):
+    t = [torch.from_numpy(np.ascontiguousarray(a)) for a in (q, k, v)]
+    return F.scaled_dot_product_attention(*t, is_causal=causal, scale=scale,
+                                          enable_gqa=gqa).numpy()
+
+
+def golden_lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                yield line
+
+
+# --------------------------------------------------------------- definition
+
+def test_probability_rows_sum_to_one_and_mask_is_exact():
+    q, k, v = rnd((2, 4, 9, 5), 1), rnd((2, 2, 9, 5), 2), rnd((2, 2, 9, 5), 3)
+    _, _, P = ao.sdpa_ref(q, k, v, 0.7, causal=True, return_probs=True)
+    assert np.abs(P.sum(-1) - 1.0).max() <= 1e-12
+    upper = np.triu(np.ones((9, 9), dtype=bool), 1)
+    assert np.all(P[..., upper] == 0.0)
+    assert np.all(P[..., ~upper] > 0.0)
+
+
+def test_causal_visibility_matches_printed_table():
+    q, k, v = rnd((1, 1, 6, 8), 4), rnd((1, 1, 6, 8), 5), rnd((1, 1, 6, 8), 6)
+    _, _, P = ao.sdpa_ref(q, k, v, 1 / math.sqrt(8), causal=True, return_probs=True)
+    for line in golden_lines("causal_rows.txt"):
+        i, cols = line.split()
+        want = [int(c) for c in cols.split(",")]
+        assert list(np.nonzero(P[0, 0, int(i)])[0]) == want
+
+
+def test_single_visible_key_returns_its_value_exactly():
+    q, k, v = rnd((2, 6, 11, 7), 7), rnd((2, 3, 11, 7), 8), rnd((2, 3, 11, 7), 9)
+    o, lse = ao.sdpa_ref(q, k, v, 0.3, causal=True)
+    for h in range(6):
+        assert np.array_equal(o[:, h, 0], v[:, h // 2, 0])
+        # lse of row 0 is the one score itself
+        assert np.allclose(lse[:, h, 0], 0.3 * np.einsum("bd,bd->b", q[:, h, 0], k[:, h // 2, 0]),
+                           atol=1e-13, rtol=0)
+
+
+def test_identical_keys_give_running_mean_of_values():
+    N = 13
+    q, v = rnd((1, 4, N, 6), 10), rnd((1, 2, N, 6), 11)
+    k = np.broadcast_to(rnd((1, 2, 1, 6), 12), (1, 2, N, 6)).copy()
+    o, lse = ao.sdpa_ref(q, k, v, 0.5, causal=True)
+    counts = np.arange(1, N + 1)[:, None]
+    for h in range(4):
+        running_mean = np.cumsum(v[0, h // 2], axis=0) / counts
+        assert np.abs(o[0, h] - running_mean).max() <= 1e-12
+        c = 0.5 * float(q[0, h, 0] @ k[0, h // 2, 0])  # score of row 0 (all equal per row)
+        s_row = 0.5 * (q[0, h] @ k[0, h // 2, 0])
+        assert np.abs(lse[0, h] - (s_row + np.log(counts[:, 0]))).max() <= 1e-12
+        assert abs(s_row[0] - c) <= 1e-15
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (6, 3), (8, 2), (4, 1)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_matches_torch_cpu_sdpa_fp64(Hq, Hkv, causal):
+    q, k, v = rnd((2, Hq, 10, 8), 20), rnd((2, Hkv, 10, 8), 21), rnd((2, Hkv, 10, 8), 22)
+    o, _ = ao.sdpa_ref(q, k, v, 1 / math.sqrt(8), causal=causal)
+    ref = torch_sdpa(q, k, v, 1 / math.sqrt(8), causal, gqa=True)
+    assert np.abs(o - ref).max() <= 1e-12
+
+
+def test_mha_endpoint_is_independent_heads():
+    q, k, v = rnd((1, 5, 9, 4), 30), rnd((1, 5, 9, 4), 31), rnd((1, 5, 9, 4), 32)
+    o, _ = ao.sdpa_ref(q, k, v, 0.5, causal=True)
+    for h in range(5):
+        ref = torch_sdpa(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], 0.5, True, gqa=False)
+        assert np.abs(o[:, h:h + 1] - ref).max() <= 1e-12
+
+
+def test_mqa_endpoint_broadcasts_the_single_kv_head():
+    q, k, v = rnd((2, 6, 9, 4), 33), rnd((2, 1, 9, 4), 34), rnd((2, 1, 9, 4), 35)
+    o, _ = ao.sdpa_ref(q, k, v, 0.5, causal=True)
+    kb, vb = np.broadcast_to(k, (2, 6, 9, 4)), np.broadcast_to(v, (2, 6, 9, 4))
+    ref = torch_sdpa(q, kb, vb, 0.5, True, gqa=False)
+    assert np.abs(o - ref).max() <= 1e-12
+
+
+def test_wrong_head_order_is_caught(monkeypatch):
+    """Plant the classic GQA bug (tile order h mod Hkv instead of repeat order
+    h // g) in the oracle and check that the library pin rejects it."""
+    q, k, v = rnd((1, 4, 7, 8), 40), rnd((1, 2, 7, 8), 41), rnd((1, 2, 7, 8), 42)
+    ref = torch_sdpa(q, k, v, 0.35, True, gqa=True)
+    good, _ = ao.sdpa_ref(q, k, v, 0.35, causal=True)
+    assert np.abs(good - ref).max() <= 1e-12
+    monkeypatch.setattr(ao, "kv_head_of", lambda h, Hq, Hkv: h % Hkv)
+    bad, _ = ao.sdpa_ref(q, k, v, 0.35, causal=True)
+    assert np.abs(bad - ref).max() > 0.1
+
+
+def test_kv_head_of_rejects_non_divisible_groups():
+    with pytest.raises(ValueError):
+        ao.kv_head_of(0, 6, 4)
+    assert [ao.kv_head_of(h, 8, 2) for h in range(8)] == [0, 0, 0, 0, 1, 1, 1, 1]
+
+
+def test_scale_is_applied_to_scores():
+    # softmax(s * c) for c -> 0 is uniform: the output becomes the running mean of V.
+    q, k, v = rnd((1, 2, 8, 4), 43), rnd((1, 2, 8, 4), 44), rnd((1, 2, 8, 4), 45)
+    o, _ = ao.sdpa_ref(q, k, v, 0.0, causal=True)
+    mean = np.cumsum(v[0], axis=1) / np.arange(1, 9)[None, :, None]
+    assert np.abs(o[0] - mean).max() <= 1e-12
+
+
+def test_shift_invariance_of_keys():
+    q, k, v = rnd((1, 4, 12, 8), 50), rnd((1, 2, 12, 8), 51) + 3.0, rnd((1, 2, 12, 8), 52)
+    o, _ = ao.sdpa_ref(q, k, v, 0.4, causal=True)
+    ks = k - k.mean(axis=2, keepdims=True)  # every score of a row shifts by q . mean(k)
+    o2, _ = ao.sdpa_ref(q, ks, v, 0.4, causal=True)
+    assert np.abs(o - o2).max() <= 1e-12
+
+
+def test_causality_rewriting_the_future_is_bit_exact():
+    q, k, v = rnd((1, 4, 16, 8), 60), rnd((1, 2, 16, 8), 61), rnd((1, 2, 16, 8), 62)
+    o, _ = ao.sdpa_ref(q, k, v, 0.3, causal=True)
+    t = 9
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    q2[:, :, t:] = rnd(q2[:, :, t:].shape, 63)
+    k2[:, :, t:] = rnd(k2[:, :, t:].shape, 64)
+    v2[:, :, t:] = rnd(v2[:, :, t:].shape, 65)
+    o2, _ = ao.sdpa_ref(q2, k2, v2, 0.3, causal=True)
+    assert np.array_equal(o[:, :, :t], o2[:, :, :t])
+    assert not np.array_equal(o[:, :, t:], o2[:, :, t:])
+
+
+# ----------------------------------------------------- online softmax pins
+
+@pytest.mark.parametrize("block", [1, 7, 23])  # 23 = N + 5, one block holds every key
+@pytest.mark.parametrize("causal", [True, False])
+def test_streaming_recurrence_equals_two_pass(block, causal):
+    q, k, v = rnd((1, 4, 18, 6), 70), rnd((1, 2, 18, 6), 71) * 3, rnd((1, 2, 18, 6), 72)
+    two_pass, _ = ao.sdpa_ref(q, k, v, 0.6, causal=causal)
+    streamed = ao.online_softmax_ref(q, k, v, 0.6, block, causal=causal)
+    assert np.abs(two_pass - streamed).max() <= 1e-12
+    ref = torch_sdpa(q, k, v, 0.6, causal, gqa=True)
+    assert np.abs(streamed - ref).max() <= 1e-12
+
+
+# ------------------------------------------------------------ sampled rows
+
+@pytest.mark.parametrize("layout", ["BNHD", "BHND"])
+def test_prefill_rows_match_library(layout):
+    qb, kb, vb = rnd((2, 6, 21, 8), 80), rnd((2, 3, 21, 8), 81), rnd((2, 3, 21, 8), 82)
+    ref = torch_sdpa(qb, kb, vb, 0.35, True, gqa=True)
+    q, k, v = (ao.from_bhnd(a, layout) for a in (qb, kb, vb))
+    samples = [(0, 0, 0), (1, 20, 5), (0, 7, 3), (1, 13, 2)]
+    rows = ao.prefill_rows_ref(torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+                               0.35, samples, layout=layout)
+    for r, (b, i, h) in zip(rows, samples):
+        assert np.abs(r - ref[b, h, i]).max() <= 1e-12
+
+
+# ------------------------------------------------------------ paged cache
+
+def test_pages_needed_and_paging_demo_numbers():
+    for line in golden_lines("paging.txt"):
+        parts = line.split()
+        if parts[0] == "blocks_needed":
+            n, bs, want = map(int, parts[1:])
+            assert ao.pages_needed(n, bs) == want
+        elif parts[0] == "demo":
+            kv = dict(p.split("=") for p in parts[1:])
+            lens = [int(x) for x in kv["lengths"].split(",")]
+            bs = int(kv["block_size"])
+            blocks = sum(ao.pages_needed(L, bs) for L in lens)
+            assert blocks == int(kv["blocks"])
+            assert blocks * bs == int(kv["slots"])
+            assert blocks * bs - sum(lens) == int(kv["waste"])
+            assert len(lens) * int(kv["max_seq_len"]) == int(kv["contiguous"])
+
+
+def test_gather_through_pages_demo_table_is_bit_exact():
+    line = [l for l in golden_lines("paging.txt") if l.startswith("tiny_pool")][0]
+    kv = dict(p.split("=") for p in line.split()[1:])
+    nb, bs, H, hd, T = (int(kv[x]) for x in ("num_blocks", "block_size", "kv_heads", "head_dim", "tokens"))
+    table = [int(x) for x in kv["table"].split(",")]
+    assert len(table) == ao.pages_needed(T, bs)
+    g = torch.Generator().manual_seed(0)
+    tokens = [torch.randn(H, hd, generator=g) for _ in range(T)]
+    pool = torch.full((nb, bs, H, hd), float("nan"))
+    for t, x in enumerate(tokens):  # append: write token t at (table[t // bs], t % bs)
+        pool[table[t // bs], t % bs] = x
+    got = ao.gather_kv_ref(pool.numpy(), table, T, bs)
+    assert np.array_equal(got, torch.stack(tokens).numpy())
+
+
+def test_gather_permuted_pool_equals_contiguous_bit_exact():
+    rng = np.random.default_rng(90)
+    L, ps, H, d = 45, 4, 3, 5
+    contiguous = rng.standard_normal((L, H, d)).astype(np.float32)
+    n = ao.pages_needed(L, ps)
+    perm = rng.permutation(20)[:n]
+    pool = np.full((20, ps, H, d), np.nan, dtype=np.float32)
+    for t in range(L):
+        pool[perm[t // ps], t % ps] = contiguous[t]
+    assert np.array_equal(ao.gather_kv_ref(pool, perm, L, ps), contiguous)
+    # a swapped pair of table entries must break the equality
+    bad = perm.copy()
+    bad[[0, 1]] = bad[[1, 0]]
+    assert not np.array_equal(ao.gather_kv_ref(pool, bad, L, ps), contiguous)
+
+
+def _paged_copy(k, v, lens, ps, seed):
+    """Scatter contiguous [B, Hkv, N, d] K/V into a permuted page pool (test helper)."""
+    B, Hkv, N, d = k.shape
+    n = [ao.pages_needed(L, ps) for L in lens]
+    total = sum(n)
+    perm = np.random.default_rng(seed).permutation(total)
+    kp = np.full((total, ps, Hkv, d), np.nan)
+    vp = np.full((total, ps, Hkv, d), np.nan)
+    table = np.full((B, max(n)), -1, dtype=np.int32)
+    c = 0
+    for b in range(B):
+        table[b, :n[b]] = perm[c:c + n[b]]
+        c += n[b]
+        for t in range(lens[b]):
+            kp[table[b, t // ps], t % ps] = k[b, :, t]
+            vp[table[b, t // ps], t % ps] = v[b, :, t]
+    return kp, vp, table
+
+
+def test_decode_through_pages_equals_prefill_row():
+    B, Hq, Hkv, N, d, ps = 2, 6, 2, 19, 8, 4
+    q, k, v = rnd((B, Hq, N, d), 100), rnd((B, Hkv, N, d), 101), rnd((B, Hkv, N, d), 102)
+    o, _ = ao.sdpa_ref(q, k, v, 0.33, causal=True)
+    for t in (0, 3, 4, 11, 18):
+        lens = [t + 1] * B
+        kp, vp, table = _paged_copy(k, v, lens, ps, seed=t)
+        dec = ao.decode_ref(q[:, :, t], kp, vp, table, np.array(lens), 0.33)
+        assert np.abs(dec - o[:, :, t]).max() <= 1e-12
+
+
+def test_decode_ragged_lengths_and_empty_sequence():
+    B, Hq, Hkv, N, d, ps = 3, 4, 1, 10, 8, 4
+    q, k, v = rnd((B, Hq, N, d), 110), rnd((B, Hkv, N, d), 111), rnd((B, Hkv, N, d), 112)
+    lens = [7, 0, 10]
+    kp, vp, table = _paged_copy(k, v, [max(L, 1) for L in lens], ps, seed=3)
+    qd = rnd((B, Hq, d), 113)
+    dec = ao.decode_ref(qd, kp, vp, table, np.array(lens), 0.5)
+    assert np.array_equal(dec[1], np.zeros((Hq, d)))  # no visible key: zero output
+    for b in (0, 2):
+        ref = torch_sdpa(qd[b][None, :, None], k[b:b + 1, :, :lens[b]], v[b:b + 1, :, :lens[b]],
+                         0.5, False, gqa=True)[0, :, 0]
+        assert np.abs(dec[b] - ref).max() <= 1e-12
+
+
+# ------------------------------------------------------------ cache sizing
+
+def test_kv_cache_bytes_matches_printed_values():
+    n = 0
+    for line in golden_lines("kv_cache_sizes.txt"):
+        L, nkv, npos, dh, b, want = map(int, line.split())
+        assert ao.kv_cache_bytes(L, nkv, npos, dh, b) == want
+        n += 1
+    assert n >= 10
+    assert oracle.kv_cache_bytes(36, 8, 131072, 64, 2) == 9 * 2 ** 30
