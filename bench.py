@@ -1,0 +1,229 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+A step is one pass of the whole path over resident inputs: the causal GQA
+prefill of the headline workload (bf16, B=4, Hq=32, Hkv=8, N=4096, d=128,
+[B,N,H,d]) followed by one paged decode step of the long-context workload
+(bf16, B=4, Hq=64, Hkv=8, d=128, seq_lens ~ U[98304, 131072], 16-token pages,
+permuted block table, split-K + LSE merge).
+
+Prints ONE JSON line. `value` is the prefill throughput in TFLOP/s under the
+causal-FLOP count (4 * B * Hq * d * N(N+1)/2 per launch, visible pairs only);
+the decode throughput (KV bytes read / time, K+V of every visible token once)
+is reported under "decode". Both are timed with HIP events recorded on the
+stream the kernels run on. The CPU baseline is the float64 oracle timed on a
+bounded sample of the same workloads on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "prefill TFLOP/s (causal GQA fwd) + decode KV-read GB/s, % of MI355X roofline"
+CSRC = os.path.join(ROOT, "exact_attention_flashattention_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def causal_flops(B, Hq, N, d) -> int:
+    return 4 * B * Hq * d * N * (N + 1) // 2
+
+
+def kv_bytes(seq_lens, Hkv, d, elem=2) -> int:
+    return int(sum(int(L) for L in seq_lens)) * Hkv * d * elem * 2
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, sources) -> float | None:
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernel source has changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != source_hash(*sources):
+        return None
+    return float(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
+
+
+def cpu_baseline(x2, x5, heads: int):
+    """Time the oracle (unchanged) on a bounded sample of both workloads."""
+    import numpy as np
+    from oracle import attention_oracle as ao
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    g = x2.Hq // x2.Hkv
+    hs = max(g, heads - heads % g)
+    q = ao.to_bhnd(x2.q[:1, :, :hs], "BNHD")
+    k = ao.to_bhnd(x2.k[:1, :, :hs // g], "BNHD")
+    v = ao.to_bhnd(x2.v[:1, :, :hs // g], "BNHD")
+    t0 = time.perf_counter()
+    ao.sdpa_ref(q, k, v, x2.scale, causal=True)
+    tp = time.perf_counter() - t0
+    pf = causal_flops(1, hs, x2.N, x2.d) / tp / 1e12
+    sel = [0]
+    t0 = time.perf_counter()
+    ao.decode_ref(x5.q[sel], x5.k_pages, x5.v_pages, x5.block_table[sel], x5.seq_lens[sel], x5.scale)
+    td = time.perf_counter() - t0
+    dg = kv_bytes(x5.seq_lens[sel].tolist(), x5.Hkv, x5.d) / td / 1e9
+    return {
+        "value": round(pf, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"prefill: batch 0, query heads 0..{hs - 1} of the headline prefill (full N={x2.N}, "
+                  f"causal-FLOP count {causal_flops(1, hs, x2.N, x2.d)}) in {tp:.2f} s; "
+                  f"decode: sequence 0 of the paged decode (L={int(x5.seq_lens[0])}) in {td:.2f} s",
+        "decode_value": round(dg, 4), "decode_unit": "GB/s",
+        "blas": "OpenBLAS (numpy)",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--skip-decode", action="store_true", help=argparse.SUPPRESS)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the kernels shard over (batch, KV head) with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import exact_attention_flashattention_amd as pkg
+    from exact_attention_flashattention_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    pkg.lib()
+    dev = torch.device("cuda:0")
+
+    log("generating inputs ...")
+    x2 = wl.workload_2()
+    x5 = wl.workload_5()
+    q, k, v = x2.q.to(dev), x2.k.to(dev), x2.v.to(dev)
+    o = torch.empty_like(q)
+    dq, dk, dv = x5.q.to(dev), x5.k_pages.to(dev), x5.v_pages.to(dev)
+    dbt, dsl = x5.block_table.to(dev), x5.seq_lens.to(dev)
+    do = torch.empty_like(dq)
+    ws_bytes = pkg.attn_decode_workspace_size(x5.B, x5.Hq, x5.Hkv, x5.d, x5.max_pages_per_seq, 0)
+    ws = torch.empty(ws_bytes // 4 + 4, dtype=torch.float32, device=dev)
+    splits = pkg.attn_decode_num_splits(x5.B, x5.Hkv, x5.max_pages_per_seq, 0)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        pkg.attn_prefill(q, k, v, o, scale=x2.scale, stream=stream)
+        if evs is not None:
+            evs[1].record(stream)
+        if not args.skip_decode:
+            pkg.attn_decode(dq, dk, dv, dbt, dsl, do, scale=x5.scale, num_splits=splits, workspace=ws,
+                            stream=stream)
+        if evs is not None:
+            evs[2].record(stream)
+
+    log(f"warmup {args.warmup} ...")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    pre_avg = sum(pre_ms) / len(pre_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+
+    flops = causal_flops(x2.B, x2.Hq, x2.N, x2.d)
+    tflops = flops / (pre_avg * 1e-3) / 1e12
+    kvb = kv_bytes(x5.seq_lens.tolist(), x5.Hkv, x5.d)
+    gbs = kvb / (dec_avg * 1e-3) / 1e9 if not args.skip_decode else None
+    log(f"prefill avg {pre_avg * 1e3:.1f} us ({tflops:.1f} TFLOP/s, min {min(pre_ms) * 1e3:.1f} us); "
+        f"decode avg {dec_avg * 1e3:.1f} us ({gbs} GB/s); wall {t_wall:.3f} s")
+
+    traffic = measured_traffic("prefill_bf16", ["prefill_bf16.hip", "attn_internal.h"])
+    dtraffic = measured_traffic("decode", ["decode.hip", "attn_internal.h"])
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": x2.name,
+            "B": x2.B, "N": x2.N, "Hq": x2.Hq, "Hkv": x2.Hkv, "d": x2.d, "causal": True,
+            "layout": "BNHD", "flops_per_launch": flops,
+            "decode_workload": x5.name,
+            "decode_seq_lens": x5.seq_lens.tolist(), "decode_num_splits": splits,
+            "step": "one prefill launch + one decode call (split kernel + merge kernel)",
+        },
+        "roofline": {
+            "bound": "mfma", "achieved": round(tflops, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "prefill_bf16_kernel<128,2,4,64>", "avg_launch_us": round(pre_avg * 1e3, 2),
+        },
+        "decode": None if args.skip_decode else {
+            "value": round(gbs, 2), "unit": "GB/s", "avg_call_us": round(dec_avg * 1e3, 2),
+            "kv_bytes_per_call": kvb,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": dtraffic,
+                         "kernel": "decode_split_kernel<128> + decode_merge_kernel<128>"},
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline(x2, x5, args.cpu_heads)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,205 @@
+"""Thin ctypes binding over libattn.so (argument marshalling only).
+
+Each function has the name of the C entry point it calls and takes torch
+tensors that already live on the GPU; every step of the computation runs in
+the library's HIP kernels. If the shared library is missing the first call
+raises ``AttnLibraryMissing``: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("ATTN_LIB", os.path.join(HERE, "libattn.so"))
+
+ATTN_OK = 0
+ATTN_F32, ATTN_BF16 = 0, 1
+ATTN_BNHD, ATTN_BHND = 0, 1
+LAYOUTS = {"BNHD": ATTN_BNHD, "BHND": ATTN_BHND}
+
+# (name, restype, argtypes) for every symbol declared in include/attn.h
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = [
+    ("attn_prefill", _i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]),
+    ("attn_prefill_ex", _i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _i, _vp]),
+    ("attn_decode_num_splits", _i, [_i, _i, _i, _i]),
+    ("attn_decode_workspace_size", _sz, [_i, _i, _i, _i, _i, _i]),
+    ("attn_decode", _i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    ("attn_gather_pages", _i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
+    ("attn_status_string", ctypes.c_char_p, [_i]),
+    ("attn_version", _i, []),
+]
+
+
+class AttnLibraryMissing(RuntimeError):
+    pass
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libattn.so once and declare every exported signature."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise AttnLibraryMissing(
+                f"{LIB_PATH} is not built; run `python -m exact_attention_flashattention_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, res, args in SIGNATURES:
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().attn_status_string(status).decode()
+
+
+attn_status_string = status_string
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _check(status: int, where: str) -> None:
+    if status != ATTN_OK:
+        raise AttnError(status, where)
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def attn_prefill_ex(q, k, v, o=None, *, causal: bool = True, scale: Optional[float] = None,
+                    layout: str = "BNHD", lse=None, stream=None):
+    """Causal (or full) GQA attention. q [B,N,Hq,d] / [B,Hq,N,d] and k, v with
+    Hkv heads, bf16 or fp32 (all alike). Returns o (allocated if not given)."""
+    import torch
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {list(LAYOUTS)}")
+    if q.dim() != 4 or k.shape != v.shape or k.dim() != 4:
+        raise ValueError("q, k, v must be 4-D and k, v alike")
+    if layout == "BNHD":
+        B, N, Hq, d = q.shape
+        Hkv = k.shape[2]
+        ok = k.shape[0] == B and k.shape[1] == N and k.shape[3] == d
+    else:
+        B, Hq, N, d = q.shape
+        Hkv = k.shape[1]
+        ok = k.shape[0] == B and k.shape[2] == N and k.shape[3] == d
+    if not ok:
+        raise ValueError(f"shape mismatch q {tuple(q.shape)} k {tuple(k.shape)}")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    dtype = {torch.bfloat16: ATTN_BF16, torch.float32: ATTN_F32}.get(q.dtype)
+    if dtype is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if o is None:
+        o = torch.empty_like(q)
+    elif o.shape != q.shape or o.dtype != q.dtype:
+        raise ValueError("o must match q")
+    if scale is None:
+        scale = d ** -0.5
+    lse_ptr = None
+    if lse is not None:
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N):
+            raise ValueError("lse must be float32 [B, Hq, N]")
+        lse_ptr = _dev(lse, "lse")
+    st = lib().attn_prefill_ex(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), lse_ptr,
+                               B, N, Hq, Hkv, d, float(scale), int(bool(causal)), dtype,
+                               LAYOUTS[layout], _stream(stream))
+    _check(st, "attn_prefill_ex")
+    return o
+
+
+def attn_prefill(q, k, v, o=None, *, causal: bool = True, scale: Optional[float] = None, stream=None):
+    """bf16 [B, N, H, d] prefill (the attn_prefill entry point)."""
+    import torch
+    if q.dtype != torch.bfloat16 or q.dim() != 4:
+        raise ValueError("attn_prefill takes bf16 [B, N, H, d] tensors")
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, N, Hkv, d) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k, v must be bf16 [B, N, Hkv, d]")
+    if o is None:
+        o = torch.empty_like(q)
+    st = lib().attn_prefill(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), B, N, Hq, Hkv, d,
+                            float(d ** -0.5 if scale is None else scale), int(bool(causal)), _stream(stream))
+    _check(st, "attn_prefill")
+    return o
+
+
+def attn_decode_num_splits(B: int, Hkv: int, max_pages_per_seq: int, num_splits: int = 0) -> int:
+    s = lib().attn_decode_num_splits(B, Hkv, max_pages_per_seq, num_splits)
+    _check(min(s, 0), "attn_decode_num_splits")
+    return s
+
+
+def attn_decode_workspace_size(B: int, Hq: int, Hkv: int, d: int, max_pages_per_seq: int,
+                               num_splits: int = 0) -> int:
+    return int(lib().attn_decode_workspace_size(B, Hq, Hkv, d, max_pages_per_seq, num_splits))
+
+
+def attn_decode(q, k_pages, v_pages, block_table, seq_lens, o=None, *, scale: Optional[float] = None,
+                num_splits: int = 0, workspace=None, stream=None):
+    """Paged decode. q [B,Hq,d] bf16; pools [num_pages,16,Hkv,d] bf16;
+    block_table int32 [B,max_pages]; seq_lens int32 [B]. Returns o [B,Hq,d]."""
+    import torch
+    if q.dtype != torch.bfloat16 or k_pages.dtype != torch.bfloat16 or v_pages.dtype != torch.bfloat16:
+        raise ValueError("decode takes bf16 q and pools")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    B, Hq, d = q.shape
+    num_pages, page_size, Hkv, d2 = k_pages.shape
+    if d2 != d or v_pages.shape != k_pages.shape:
+        raise ValueError("pool shape mismatch")
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_table must be [B, max_pages] and seq_lens [B]")
+    mpps = block_table.shape[1]
+    if o is None:
+        o = torch.empty_like(q)
+    need = attn_decode_workspace_size(B, Hq, Hkv, d, mpps, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().attn_decode(_dev(q, "q"), _dev(k_pages, "k_pages"), _dev(v_pages, "v_pages"),
+                           _dev(block_table, "block_table"), _dev(seq_lens, "seq_lens"), _dev(o, "o"),
+                           B, Hq, Hkv, d, page_size, mpps, num_pages,
+                           float(d ** -0.5 if scale is None else scale), num_splits,
+                           _dev(workspace, "workspace"), ws_bytes, _stream(stream))
+    _check(st, "attn_decode")
+    return o
+
+
+def attn_gather_pages(pages, block_table, seq_lens, max_len: int, out=None, stream=None):
+    """Materialise [B, max_len, Hkv, d] from a page pool through the block table."""
+    import torch
+    num_pages, page_size, Hkv, d = pages.shape
+    B = block_table.shape[0]
+    if out is None:
+        out = torch.zeros((B, max_len, Hkv, d), dtype=pages.dtype, device=pages.device)
+    st = lib().attn_gather_pages(_dev(pages, "pages"), _dev(block_table, "block_table"),
+                                 _dev(seq_lens, "seq_lens"), _dev(out, "out"), B, Hkv, d, page_size,
+                                 block_table.shape[1], num_pages, max_len, pages.element_size(),
+                                 _stream(stream))
+    _check(st, "attn_gather_pages")
+    return out

@@ -1,0 +1,154 @@
+// C-ABI entry points: argument validation on the host, then kernel launches.
+// Every check happens before anything is enqueued, so an error status means
+// no kernel ran and no output was touched.
+#include "../../include/attn.h"
+#include "attn_internal.h"
+
+#include <math.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr long long kMaxElems = 1LL << 40;  // sanity bound on any one tensor
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_heads(int Hq, int Hkv) {
+  if (Hq < 1 || Hkv < 1) return ATTN_ERR_SHAPE;
+  if (Hq % Hkv) return ATTN_ERR_GQA;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_NULL: return "ATTN_ERR_NULL: a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "ATTN_ERR_SHAPE: invalid size or scale";
+    case ATTN_ERR_GQA: return "ATTN_ERR_GQA: Hq is not a multiple of Hkv";
+    case ATTN_ERR_HEAD_DIM: return "ATTN_ERR_HEAD_DIM: head dimension must be 64 or 128";
+    case ATTN_ERR_DTYPE: return "ATTN_ERR_DTYPE: unsupported element type";
+    case ATTN_ERR_LAYOUT: return "ATTN_ERR_LAYOUT: unsupported layout";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace missing or too small";
+    case ATTN_ERR_ALIGN: return "ATTN_ERR_ALIGN: tensor pointer not 16-byte aligned";
+    case ATTN_ERR_LAUNCH: return "ATTN_ERR_LAUNCH: kernel launch failed";
+    case ATTN_ERR_PAGE: return "ATTN_ERR_PAGE: page_size must be 16";
+    default: return "unknown attn status";
+  }
+}
+
+int attn_prefill_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int N, int Hq, int Hkv, int d, float scale, int causal,
+                    int dtype, int layout, void* stream) {
+  if (!q || !k || !v || !o) return ATTN_ERR_NULL;
+  if (B < 1 || N < 1) return ATTN_ERR_SHAPE;
+  int st = check_heads(Hq, Hkv);
+  if (st) return st;
+  if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (layout != ATTN_BNHD && layout != ATTN_BHND) return ATTN_ERR_LAYOUT;
+  if (!isfinite(scale)) return ATTN_ERR_SHAPE;
+  if ((long long)B * N * Hq * d > kMaxElems) return ATTN_ERR_SHAPE;
+  if (dtype == ATTN_F32 && (Hq > 65535 || B > 65535)) return ATTN_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_ALIGN;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_ALIGN;
+
+  attn::PrefillParams p;
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.B = B; p.N = N; p.Hq = Hq; p.Hkv = Hkv;
+  const long long D = d;
+  if (layout == ATTN_BNHD) {
+    p.q_sb = (long long)N * Hq * D; p.q_sn = Hq * D; p.q_sh = D;
+    p.k_sb = (long long)N * Hkv * D; p.k_sn = Hkv * D; p.k_sh = D;
+  } else {
+    p.q_sb = (long long)Hq * N * D; p.q_sn = D; p.q_sh = (long long)N * D;
+    p.k_sb = (long long)Hkv * N * D; p.k_sn = D; p.k_sh = (long long)N * D;
+  }
+  p.o_sb = p.q_sb; p.o_sn = p.q_sn; p.o_sh = p.q_sh;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.causal = causal ? 1 : 0;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = dtype == ATTN_BF16 ? attn::launch_prefill_bf16(p, d, s)
+                                          : attn::launch_prefill_f32(p, d, s);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_prefill(const void* q, const void* k, const void* v, void* o,
+                 int B, int N, int Hq, int Hkv, int d, float scale, int causal, void* stream) {
+  return attn_prefill_ex(q, k, v, o, nullptr, B, N, Hq, Hkv, d, scale, causal, ATTN_BF16,
+                         ATTN_BNHD, stream);
+}
+
+int attn_decode_num_splits(int B, int Hkv, int max_pages_per_seq, int num_splits) {
+  if (B < 1 || Hkv < 1 || max_pages_per_seq < 1 || num_splits < 0) return ATTN_ERR_SHAPE;
+  if (num_splits > 0) return num_splits < max_pages_per_seq ? num_splits : max_pages_per_seq;
+  return attn::auto_decode_splits(B, Hkv, max_pages_per_seq);
+}
+
+size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int d, int max_pages_per_seq,
+                                  int num_splits) {
+  if (check_heads(Hq, Hkv) || (d != 64 && d != 128)) return 0;
+  const int S = attn_decode_num_splits(B, Hkv, max_pages_per_seq, num_splits);
+  if (S < 1) return 0;
+  return (size_t)B * Hq * S * (d + 2) * sizeof(float);
+}
+
+int attn_decode(const void* q, const void* k_pages, const void* v_pages,
+                const int32_t* block_table, const int32_t* seq_lens, void* o,
+                int B, int Hq, int Hkv, int d, int page_size, int max_pages_per_seq,
+                int num_pages, float scale, int num_splits,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !o) return ATTN_ERR_NULL;
+  if (B < 1 || max_pages_per_seq < 1 || num_pages < 1 || num_splits < 0) return ATTN_ERR_SHAPE;
+  int st = check_heads(Hq, Hkv);
+  if (st) return st;
+  if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  if (page_size != 16) return ATTN_ERR_PAGE;
+  if (!isfinite(scale)) return ATTN_ERR_SHAPE;
+  if ((long long)max_pages_per_seq * page_size > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  if ((long long)num_pages * page_size * Hkv * d > kMaxElems) return ATTN_ERR_SHAPE;
+  if ((long long)B * max_pages_per_seq > kMaxElems) return ATTN_ERR_SHAPE;
+  const int S = attn_decode_num_splits(B, Hkv, max_pages_per_seq, num_splits);
+  const size_t need = attn_decode_workspace_size(B, Hq, Hkv, d, max_pages_per_seq, num_splits);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o) ||
+      !aligned16(workspace) || (reinterpret_cast<uintptr_t>(block_table) & 3u) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return ATTN_ERR_ALIGN;
+
+  attn::DecodeParams p;
+  p.q = q; p.k_pages = k_pages; p.v_pages = v_pages;
+  p.block_table = block_table; p.seq_lens = seq_lens; p.o = o;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_ml = p.ws_o + (size_t)B * Hq * S * d;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.max_pages_per_seq = max_pages_per_seq;
+  p.num_splits = S;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  const hipError_t e = attn::launch_decode(p, d, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_gather_pages(const void* pages, const int32_t* block_table, const int32_t* seq_lens,
+                      void* out, int B, int Hkv, int d, int page_size, int max_pages_per_seq,
+                      int num_pages, int max_len, int elem_bytes, void* stream) {
+  if (!pages || !block_table || !seq_lens || !out) return ATTN_ERR_NULL;
+  if (B < 1 || B > 65535 || Hkv < 1 || d < 1 || max_pages_per_seq < 1 || num_pages < 1 ||
+      max_len < 1)
+    return ATTN_ERR_SHAPE;
+  if (page_size != 16) return ATTN_ERR_PAGE;
+  if (elem_bytes != 2 && elem_bytes != 4) return ATTN_ERR_DTYPE;
+  if (((long long)Hkv * d * elem_bytes) % 4) return ATTN_ERR_SHAPE;
+  if (!aligned16(pages) || !aligned16(out)) return ATTN_ERR_ALIGN;
+  const hipError_t e = attn::launch_gather(pages, block_table, seq_lens, out, B, Hkv, d, page_size,
+                                           max_pages_per_seq, max_len, elem_bytes,
+                                           reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Internal interface between the C-ABI shim (attn_abi.hip) and the kernel
+// launchers. Nothing here is exported from the shared library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// One prefill problem. Strides are in elements; v shares k's strides.
+struct PrefillParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;  // optional [B, Hq, N] natural-log LSE
+  int B, N, Hq, Hkv;
+  long long q_sb, q_sn, q_sh;
+  long long k_sb, k_sn, k_sh;
+  long long o_sb, o_sn, o_sh;
+  float scale_log2;  // scale * log2(e): scores are carried in base-2 units
+  int causal;
+};
+
+// One decode problem (bf16 pages, page_size 16).
+struct DecodeParams {
+  const void* q;        // [B, Hq, d]
+  const void* k_pages;  // [num_pages, 16, Hkv, d]
+  const void* v_pages;
+  const int32_t* block_table;  // [B, max_pages_per_seq]
+  const int32_t* seq_lens;     // [B]
+  void* o;                     // [B, Hq, d]
+  float* ws_ml;                // [B, Hq, splits, 2]   (m in base-2 units, l)
+  float* ws_o;                 // [B, Hq, splits, d]   unnormalised partial outputs
+  int B, Hq, Hkv, max_pages_per_seq, num_splits;
+  float scale_log2;
+};
+
+hipError_t launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream);
+hipError_t launch_prefill_f32(const PrefillParams& p, int d, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t stream);
+hipError_t launch_gather(const void* pages, const int32_t* block_table,
+                         const int32_t* seq_lens, void* out, int B, int Hkv, int d,
+                         int page_size, int max_pages_per_seq, int max_len,
+                         int elem_bytes, hipStream_t stream);
+
+// Split count chosen when the caller passes 0: enough (sequence, KV head,
+// split) work-groups to give every compute unit several, with at least 8
+// pages per split.
+int auto_decode_splits(int B, int Hkv, int max_pages_per_seq);
+
+}  // namespace attn

@@ -1,0 +1,197 @@
+/*
+ * attn.h - exact scaled-dot-product attention for AMD MI355X (gfx950 / CDNA4).
+ *
+ * Two entry points compute softmax(Q K^T * scale + M) V exactly, in the
+ * FlashAttention style (key tiles, online softmax, no N x N matrix in memory):
+ *
+ *   attn_prefill / attn_prefill_ex : causal (or full) self-attention over a
+ *       whole sequence, grouped-query heads (MHA, GQA and MQA by one Hkv dial).
+ *   attn_decode : one new query token per sequence against a KV cache stored in
+ *       fixed-size pages addressed through a block table, split along the
+ *       context and merged by log-sum-exp.
+ *
+ * Definitions follow these pages (cited by title and section):
+ *   [SDPA]  "Module 5. Modern Attention Mechanisms" (vladkulikov.com), section 4
+ *           "SDPA, masks, and the square-root scale" (the operator, the additive
+ *           0/-inf mask, causality p_k <= p_q, the empty-row policy) and
+ *           section 6 "GQA is a grouping invariant" (query head h reads KV head
+ *           floor(h / (Hq/Hkv)); Hq must be a multiple of Hkv).
+ *   [FA]    "inference-attention" (brunomaga.github.io), section "FlashAttention"
+ *           (running max m, running sum l, unnormalised O rescaled by e^(m-m'),
+ *           output O / l; tiles entirely above the diagonal are skipped) and
+ *           section "FlashDecoding" (split the cached keys and values along the
+ *           sequence, each chunk yields a partial output with its max and sum,
+ *           a final reduction combines them with the same rescaling).
+ *   [PAGED] "Module 09: Efficient Attention" (learnllm.pages.dev), section "Paged
+ *           Attention: The KV Cache as Virtual Memory", subsection "Code: A
+ *           Paged KV Cache from Scratch": pool (num_blocks, block_size,
+ *           num_kv_heads, head_dim); token t of a sequence is at
+ *           (block_table[t / block_size], t % block_size).
+ *   [KV]    "USAAIO Lesson 90" (naruhodotutoring.com), KV-cache worked example:
+ *           a decode step appends its own K/V, then its query attends over
+ *           every cached key including itself.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     allocates no device memory, keeps no pointer after the call returns and
+ *     has no global state. Calls are thread-safe.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). The
+ *     call validates its arguments on the host, enqueues its kernels on
+ *     `stream` and returns without synchronising. Errors inside kernels (a
+ *     device fault) surface at the caller's next synchronisation.
+ *   - On any non-zero status nothing has been enqueued and no output has been
+ *     written. No C++ exception crosses this interface.
+ *   - Every tensor pointer must be 16-byte aligned and dense (no padding
+ *     between rows) in the layout stated.
+ *   - bf16 is the bfloat16 storage format (1 sign, 8 exponent, 7 mantissa
+ *     bits). Products are accumulated in fp32; outputs are rounded to
+ *     nearest-even once.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (0 = success, negative = error). */
+enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = -1,       /* a required pointer is NULL */
+    ATTN_ERR_SHAPE = -2,      /* a size is <= 0 (or < 0 where 0 is allowed), a size
+                                 product overflows, or scale is not finite */
+    ATTN_ERR_GQA = -3,        /* Hq is not a multiple of Hkv */
+    ATTN_ERR_HEAD_DIM = -4,   /* d is not 64 or 128 */
+    ATTN_ERR_DTYPE = -5,      /* unsupported dtype code */
+    ATTN_ERR_LAYOUT = -6,     /* unsupported layout code */
+    ATTN_ERR_WORKSPACE = -7,  /* workspace too small (or NULL when needed) */
+    ATTN_ERR_ALIGN = -8,      /* a tensor pointer is not 16-byte aligned */
+    ATTN_ERR_LAUNCH = -9,     /* the HIP runtime refused a launch */
+    ATTN_ERR_PAGE = -10       /* page_size is not 16 */
+};
+
+/* Element types. */
+enum { ATTN_F32 = 0, ATTN_BF16 = 1 };
+
+/* Prefill layouts for q, k, v and o (the head axis holds Hq heads for q and o,
+ * Hkv heads for k and v):
+ *   ATTN_BNHD : [B, N, H, d]  token-major (row (b, n) holds all heads)
+ *   ATTN_BHND : [B, H, N, d]  head-major                                   */
+enum { ATTN_BNHD = 0, ATTN_BHND = 1 };
+
+/*
+ * attn_prefill - causal GQA attention over whole sequences, bf16, [B, N, H, d].
+ *
+ * q: [B, N, Hq, d] bf16;  k, v: [B, N, Hkv, d] bf16;  o: [B, N, Hq, d] bf16 (out).
+ * For batch b, query head h and query position i:
+ *   o[b,i,h,:] = sum_j P_ij v[b,j,kv,:],  P_i = softmax_j(scale * q[b,i,h,:].k[b,j,kv,:] + M_ij)
+ * with kv = floor(h / (Hq/Hkv)) [SDPA section 6] and M_ij = 0 if (causal == 0 or
+ * j <= i) else -inf [SDPA section 4]. Queries and keys share the origin
+ * (N_q = N_k = N), so every row has at least one visible key. Requires
+ * B, N, Hq, Hkv >= 1, d in {64, 128}, finite scale (1/sqrt(d) is the usual
+ * choice). Equivalent to attn_prefill_ex(..., lse = NULL, ATTN_BF16, ATTN_BNHD).
+ */
+int attn_prefill(const void* q, const void* k, const void* v, void* o,
+                 int B, int N, int Hq, int Hkv, int d, float scale, int causal,
+                 void* stream);
+
+/*
+ * attn_prefill_ex - as attn_prefill, with the element type, the layout and an
+ * optional log-sum-exp output made explicit.
+ *
+ * dtype:  ATTN_BF16 (bf16 in, fp32 accumulation, bf16 out, MFMA path) or
+ *         ATTN_F32 (fp32 in, fp32 arithmetic, fp32 out).
+ * layout: ATTN_BNHD or ATTN_BHND, applied to q, k, v and o alike.
+ * lse:    NULL, or fp32 [B, Hq, N] (out): the natural logarithm of each row's
+ *         softmax denominator, max_j s_ij + ln(sum_j e^(s_ij - max)), where
+ *         s_ij = scale * q_i . k_j over the visible keys.
+ */
+int attn_prefill_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int N, int Hq, int Hkv, int d, float scale, int causal,
+                    int dtype, int layout, void* stream);
+
+/*
+ * attn_decode_num_splits - the number of context splits attn_decode uses.
+ *
+ * num_splits > 0 is returned unchanged (clamped to max_pages_per_seq); 0 asks
+ * for the automatic choice, which depends only on the arguments given here
+ * (not on the device), so that a result can be reproduced exactly. Returns
+ * a negative status for invalid sizes.
+ */
+int attn_decode_num_splits(int B, int Hkv, int max_pages_per_seq, int num_splits);
+
+/*
+ * attn_decode_workspace_size - bytes of fp32 scratch attn_decode needs for
+ * (B, Hq, d, num_splits) after resolving num_splits with
+ * attn_decode_num_splits: B*Hq*num_splits*(d + 2)*4. Returns 0 for invalid sizes.
+ */
+size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int d, int max_pages_per_seq,
+                                  int num_splits);
+
+/*
+ * attn_decode - one query token per sequence against a paged KV cache, bf16.
+ *
+ * q:           [B, Hq, d] bf16, the query of the newest token of each sequence.
+ * k_pages,
+ * v_pages:     [num_pages, page_size, Hkv, d] bf16, the physical page pool
+ *              [PAGED]; a page holds page_size consecutive tokens of one
+ *              sequence, every KV head.
+ * block_table: int32 [B, max_pages_per_seq] (device). Entry p of row b is the
+ *              physical page holding tokens p*page_size .. p*page_size +
+ *              page_size - 1 of sequence b. Entries past a sequence's last page
+ *              are never read.
+ * seq_lens:    int32 [B] (device), tokens cached per sequence, including the
+ *              newest token (its K/V already written) [KV].
+ * o:           [B, Hq, d] bf16 (out).
+ * For sequence b with L = seq_lens[b] and query head h:
+ *   o[b,h,:] = sum_{t<L} P_t v_t,  P = softmax_t(scale * q[b,h,:].k_t),
+ * with k_t = k_pages[block_table[b, t/page_size], t%page_size, kv, :] (and v_t
+ * alike), kv = floor(h / (Hq/Hkv)). A sequence with L == 0 has no visible key
+ * and gets o[b] = 0 (the zero-output policy of [SDPA] section 4).
+ * The context of each sequence is cut into num_splits contiguous ranges of
+ * logical pages; each range yields a partial (max, sum, unnormalised output)
+ * in `workspace`, and a second kernel merges them by log-sum-exp [FA,
+ * FlashDecoding]. The split boundaries depend only on L and num_splits, so the
+ * result does not depend on where the pages sit in the pool: a permuted block
+ * table gives output bit-identical to the identity table.
+ *
+ * Preconditions checked on the device side only by the caller:
+ *   0 <= seq_lens[b] <= max_pages_per_seq * page_size, and every table entry
+ *   that is read lies in [0, num_pages). Violations read out of bounds.
+ * Requires page_size == 16, d in {64, 128}, Hq a multiple of Hkv,
+ * workspace_bytes >= attn_decode_workspace_size(...). The workspace is caller
+ * owned; calls that overlap in time must not share one.
+ */
+int attn_decode(const void* q, const void* k_pages, const void* v_pages,
+                const int32_t* block_table, const int32_t* seq_lens, void* o,
+                int B, int Hq, int Hkv, int d, int page_size, int max_pages_per_seq,
+                int num_pages, float scale, int num_splits,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_gather_pages - materialise the logical cache of each sequence from the
+ * page pool, with the same address computation attn_decode uses [PAGED].
+ *
+ * pages: [num_pages, page_size, Hkv, d] of elem_bytes-sized elements (2 or 4);
+ * out:   [B, max_len, Hkv, d] (out); row t of sequence b receives token t for
+ *        t < min(seq_lens[b], max_len); other rows are left untouched.
+ * A test aid: it moves bytes only, so its result is bit-exact.
+ */
+int attn_gather_pages(const void* pages, const int32_t* block_table, const int32_t* seq_lens,
+                      void* out, int B, int Hkv, int d, int page_size, int max_pages_per_seq,
+                      int num_pages, int max_len, int elem_bytes, void* stream);
+
+/* attn_status_string - a static, human-readable name for a status code. */
+const char* attn_status_string(int status);
+
+/* attn_version - library version, major*10000 + minor*100 + patch. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

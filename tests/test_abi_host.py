@@ -1,0 +1,133 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects invalid arguments on the host with the documented
+status codes before any launch (so no kernel runs in these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_attention_flashattention_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def header_enum(name):
+    text = open(HEADER).read()
+    m = re.search(rf"\b{name}\s*=\s*(-?\d+)", text)
+    return int(m.group(1))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return binding.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = header_functions()
+    assert len(names) == 8
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(n for n, _, _ in binding.SIGNATURES) == names
+
+
+def test_status_strings_and_version(L):
+    for code in range(0, -11, -1):
+        s = binding.status_string(code)
+        assert s and "unknown" not in s
+    assert "unknown" in binding.status_string(-99)
+    assert L.attn_version() >= 10000
+
+
+# Host buffers stand in for device pointers: every call below fails validation
+# before anything touches the GPU.
+BUF = (ctypes.c_uint8 * 4096)()
+A = (ctypes.addressof(BUF) + 15) & ~15
+ERR = {n: header_enum(n) for n in ("ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_GQA", "ATTN_ERR_HEAD_DIM",
+                                  "ATTN_ERR_DTYPE", "ATTN_ERR_LAYOUT", "ATTN_ERR_WORKSPACE",
+                                  "ATTN_ERR_ALIGN", "ATTN_ERR_PAGE")}
+
+
+def prefill(L, **kw):
+    a = dict(q=A, k=A, v=A, o=A, lse=None, B=1, N=8, Hq=4, Hkv=2, d=64, scale=0.125, causal=1,
+             dtype=1, layout=0)
+    a.update(kw)
+    return L.attn_prefill_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["N"], a["Hq"], a["Hkv"],
+                             a["d"], a["scale"], a["causal"], a["dtype"], a["layout"], None)
+
+
+@pytest.mark.parametrize("kw,err", [
+    (dict(q=None), "ATTN_ERR_NULL"), (dict(o=None), "ATTN_ERR_NULL"),
+    (dict(B=0), "ATTN_ERR_SHAPE"), (dict(N=-1), "ATTN_ERR_SHAPE"), (dict(Hkv=0), "ATTN_ERR_SHAPE"),
+    (dict(Hq=6, Hkv=4), "ATTN_ERR_GQA"), (dict(d=96), "ATTN_ERR_HEAD_DIM"), (dict(d=256), "ATTN_ERR_HEAD_DIM"),
+    (dict(dtype=7), "ATTN_ERR_DTYPE"), (dict(layout=3), "ATTN_ERR_LAYOUT"),
+    (dict(scale=float("nan")), "ATTN_ERR_SHAPE"), (dict(scale=float("inf")), "ATTN_ERR_SHAPE"),
+    (dict(q=A + 2), "ATTN_ERR_ALIGN"), (dict(v=A + 8), "ATTN_ERR_ALIGN"), (dict(lse=A + 1), "ATTN_ERR_ALIGN"),
+    (dict(B=1 << 20, N=1 << 20, Hq=64, Hkv=8), "ATTN_ERR_SHAPE"),
+])
+def test_prefill_rejects(L, kw, err):
+    assert prefill(L, **kw) == ERR[err]
+
+
+def test_prefill_plain_entry_validates(L):
+    assert L.attn_prefill(A, A, A, A, 1, 8, 4, 3, 64, 0.125, 1, None) == ERR["ATTN_ERR_GQA"]
+    assert L.attn_prefill(A, None, A, A, 1, 8, 4, 2, 64, 0.125, 1, None) == ERR["ATTN_ERR_NULL"]
+
+
+def decode(L, **kw):
+    a = dict(q=A, k=A, v=A, table=A, lens=A, o=A, B=2, Hq=8, Hkv=2, d=128, page_size=16, mpps=4,
+             num_pages=8, scale=0.1, splits=0, ws=A, ws_bytes=1 << 30)
+    a.update(kw)
+    return L.attn_decode(a["q"], a["k"], a["v"], a["table"], a["lens"], a["o"], a["B"], a["Hq"], a["Hkv"],
+                         a["d"], a["page_size"], a["mpps"], a["num_pages"], a["scale"], a["splits"],
+                         a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,err", [
+    (dict(q=None), "ATTN_ERR_NULL"), (dict(table=None), "ATTN_ERR_NULL"), (dict(lens=None), "ATTN_ERR_NULL"),
+    (dict(B=0), "ATTN_ERR_SHAPE"), (dict(mpps=0), "ATTN_ERR_SHAPE"), (dict(num_pages=0), "ATTN_ERR_SHAPE"),
+    (dict(splits=-1), "ATTN_ERR_SHAPE"), (dict(Hq=8, Hkv=3), "ATTN_ERR_GQA"), (dict(d=32), "ATTN_ERR_HEAD_DIM"),
+    (dict(page_size=8), "ATTN_ERR_PAGE"), (dict(scale=float("nan")), "ATTN_ERR_SHAPE"),
+    (dict(ws=None), "ATTN_ERR_WORKSPACE"), (dict(ws_bytes=16), "ATTN_ERR_WORKSPACE"),
+    (dict(k=A + 4), "ATTN_ERR_ALIGN"), (dict(table=A + 2), "ATTN_ERR_ALIGN"),
+    (dict(mpps=1 << 28), "ATTN_ERR_SHAPE"),
+])
+def test_decode_rejects(L, kw, err):
+    assert decode(L, **kw) == ERR[err]
+
+
+def test_split_count_and_workspace_size(L):
+    # explicit counts are clamped to the page count; 0 picks a device-independent value
+    assert L.attn_decode_num_splits(4, 8, 100, 7) == 7
+    assert L.attn_decode_num_splits(4, 8, 5, 7) == 5
+    auto = L.attn_decode_num_splits(4, 8, 8192, 0)
+    assert 1 <= auto <= 8192 // 8
+    assert L.attn_decode_num_splits(64, 8, 512, 0) >= 1
+    assert L.attn_decode_num_splits(0, 8, 512, 0) == ERR["ATTN_ERR_SHAPE"]
+    assert L.attn_decode_workspace_size(4, 64, 8, 128, 8192, 0) == 4 * 64 * auto * 130 * 4
+    assert L.attn_decode_workspace_size(4, 64, 8, 128, 8192, 3) == 4 * 64 * 3 * 130 * 4
+    assert L.attn_decode_workspace_size(4, 64, 7, 128, 8192, 3) == 0
+    assert L.attn_decode_workspace_size(4, 64, 8, 96, 8192, 3) == 0
+
+
+def test_gather_rejects(L):
+    g = L.attn_gather_pages
+    assert g(None, A, A, A, 1, 2, 64, 16, 4, 8, 10, 2, None) == ERR["ATTN_ERR_NULL"]
+    assert g(A, A, A, A, 1, 2, 64, 8, 4, 8, 10, 2, None) == ERR["ATTN_ERR_PAGE"]
+    assert g(A, A, A, A, 1, 2, 64, 16, 4, 8, 10, 3, None) == ERR["ATTN_ERR_DTYPE"]
+    assert g(A, A, A, A, 0, 2, 64, 16, 4, 8, 10, 2, None) == ERR["ATTN_ERR_SHAPE"]
+    assert g(A + 4, A, A, A, 1, 2, 64, 16, 4, 8, 10, 2, None) == ERR["ATTN_ERR_ALIGN"]
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding.attn_prefill(x, x, x, o=torch.empty_like(x))

@@ -1,0 +1,177 @@
+"""Prefill parity on the GPU: the HIP path (through the C ABI) against the CPU
+float64 oracle, element by element on small and ragged shapes, on sampled rows
+at the full workload sizes, plus bit-exact properties (row 0, causality,
+determinism).
+
+Tolerances (written here, applied to every comparison against the fp64
+oracle's unrounded output): fp32 inputs max-abs <= 1e-5; bf16 inputs with fp32
+accumulation max-abs <= 2e-2 and mean-abs <= 5e-3.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_flashattention_amd import binding as bd
+from exact_attention_flashattention_amd import workloads as wl
+from oracle import attention_oracle as ao
+
+pytestmark = pytest.mark.gpu
+
+F32_MAX = 1e-5
+BF16_MAX, BF16_MEAN = 2e-2, 5e-3
+LSE_BF16 = 1e-2
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run(x: wl.PrefillInputs, lse=False):
+    q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+    l = torch.full((x.B, x.Hq, x.N), float("nan"), device="cuda") if lse else None
+    o = bd.attn_prefill_ex(q, k, v, causal=x.causal, scale=x.scale, layout=x.layout, lse=l)
+    torch.cuda.synchronize()
+    return (o.cpu(), l.cpu() if lse else None)
+
+
+def oracle(x: wl.PrefillInputs):
+    o, lse = ao.sdpa_ref(ao.to_bhnd(x.q, x.layout), ao.to_bhnd(x.k, x.layout), ao.to_bhnd(x.v, x.layout),
+                         x.scale, causal=x.causal)
+    return ao.from_bhnd(o, x.layout), lse
+
+
+def errs(got, ref):
+    e = np.abs(got.double().numpy() - ref)
+    return float(e.max()), float(e.mean())
+
+
+def test_workload_1_fp32():
+    x = wl.workload_1()
+    log(f"case: {x.name}")
+    got, lse = run(x, lse=True)
+    ref, ref_lse = oracle(x)
+    mx, mean = errs(got, ref)
+    log(f"  max-abs {mx:.3e} mean-abs {mean:.3e}")
+    assert mx <= F32_MAX
+    assert np.abs(lse.double().numpy() - ref_lse).max() <= F32_MAX
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("layout", ["BNHD", "BHND"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp32_small(d, layout, causal):
+    x = wl.prefill_inputs(2, 77, 6, 3, d, seed=300 + d, dtype=torch.float32, layout=layout, causal=causal)
+    got, lse = run(x, lse=True)
+    ref, ref_lse = oracle(x)
+    mx, _ = errs(got, ref)
+    assert mx <= F32_MAX
+    assert np.abs(lse.double().numpy() - ref_lse).max() <= F32_MAX
+
+
+BF16_CASES = [
+    # B, N, Hq, Hkv, d
+    (1, 1, 4, 2, 128),     # a single token
+    (2, 7, 4, 4, 64),      # shorter than one key tile
+    (1, 64, 8, 2, 128),    # exactly one key tile
+    (2, 100, 4, 1, 64),    # ragged, MQA
+    (1, 256, 8, 8, 128),   # exactly one query tile, MHA
+    (2, 257, 8, 2, 128),   # one past a query tile
+    (1, 333, 6, 3, 64),    # ragged, several tiles
+    (1, 600, 4, 2, 128),   # several query tiles, ragged tail
+]
+
+
+@pytest.mark.parametrize("shape", BF16_CASES)
+@pytest.mark.parametrize("layout", ["BNHD", "BHND"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_bf16_small(shape, layout, causal):
+    B, N, Hq, Hkv, d = shape
+    x = wl.prefill_inputs(B, N, Hq, Hkv, d, seed=1000 + N + d, layout=layout, causal=causal)
+    log(f"case: bf16 B={B} N={N} Hq={Hq} Hkv={Hkv} d={d} {layout} causal={causal}")
+    got, lse = run(x, lse=True)
+    ref, ref_lse = oracle(x)
+    mx, mean = errs(got, ref)
+    log(f"  max-abs {mx:.3e} mean-abs {mean:.3e}")
+    assert mx <= BF16_MAX and mean <= BF16_MEAN
+    assert np.abs(lse.double().numpy() - ref_lse).max() <= LSE_BF16
+
+
+def test_plain_entry_point_matches_ex():
+    x = wl.prefill_inputs(2, 300, 8, 2, 128, seed=5)
+    q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+    a = bd.attn_prefill(q, k, v)
+    b = bd.attn_prefill_ex(q, k, v, causal=True, layout="BNHD")
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_row_zero_is_v0_bit_exact():
+    x = wl.prefill_inputs(2, 300, 8, 2, 128, seed=6)
+    got, _ = run(x)
+    g = x.Hq // x.Hkv
+    for h in range(x.Hq):
+        assert torch.equal(got[:, 0, h], x.v[:, 0, h // g])
+
+
+def test_causality_bit_exact():
+    x = wl.prefill_inputs(1, 520, 8, 2, 128, seed=7)
+    a, _ = run(x)
+    t = 300
+    y = wl.prefill_inputs(1, 520, 8, 2, 128, seed=8)
+    x2 = wl.PrefillInputs(x.q.clone(), x.k.clone(), x.v.clone(), *[getattr(x, f) for f in
+                          ("B", "N", "Hq", "Hkv", "d", "scale", "causal", "layout")])
+    x2.q[:, t:] = y.q[:, t:]
+    x2.k[:, t:] = y.k[:, t:]
+    x2.v[:, t:] = y.v[:, t:]
+    b, _ = run(x2)
+    assert torch.equal(a[:, :t], b[:, :t])
+    assert not torch.equal(a[:, t:], b[:, t:])
+
+
+def test_deterministic():
+    x = wl.prefill_inputs(2, 1000, 8, 2, 128, seed=9)
+    a, _ = run(x)
+    b, _ = run(x)
+    assert torch.equal(a, b)
+
+
+def sample_rows(x, n, seed):
+    rng = np.random.default_rng(seed)
+    picks = {(0, 0, 0), (x.B - 1, x.N - 1, x.Hq - 1), (0, 1, 1), (0, x.N // 2, 0)}
+    for i in (63, 64, 127, 128, 255, 256, 257, 511, 512, 1023, 2047, 2048, 4095):
+        if i < x.N:
+            picks.add((int(rng.integers(x.B)), i, int(rng.integers(x.Hq))))
+    while len(picks) < n:
+        picks.add((int(rng.integers(x.B)), int(rng.integers(x.N)), int(rng.integers(x.Hq))))
+    return sorted(picks)
+
+
+def full_size_check(x, n_samples=96):
+    log(f"case: {x.name}")
+    q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+    o = bd.attn_prefill_ex(q, k, v, causal=True, scale=x.scale, layout=x.layout)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o.float()).all())
+    g = x.Hq // x.Hkv
+    o0 = o[:, 0].cpu()
+    for h in range(x.Hq):
+        assert torch.equal(o0[:, h], x.v[:, 0, h // g])
+    samples = sample_rows(x, n_samples, seed=x.N)
+    ref = ao.prefill_rows_ref(x.q, x.k, x.v, x.scale, samples, layout=x.layout)
+    got = torch.stack([o[b, i, h] for (b, i, h) in samples]).cpu()
+    mx, mean = errs(got, ref)
+    log(f"  sampled {len(samples)} rows: max-abs {mx:.3e} mean-abs {mean:.3e}")
+    assert mx <= BF16_MAX and mean <= BF16_MEAN
+
+
+def test_workload_2_full_size_sampled():
+    full_size_check(wl.workload_2())
+
+
+@pytest.mark.parametrize("hkv", [16, 1])
+def test_workload_3_full_size_sampled(hkv):
+    full_size_check(wl.workload_3(hkv))
