@@ -101,6 +101,47 @@ def cpu_baseline(x2, x5, heads: int):
     }
 
 
+def only(args, dev) -> int:
+    """Launch one kernel kind warmup + steps times and report its event time."""
+    import torch
+    import exact_attention_flashattention_amd as pkg
+    from exact_attention_flashattention_amd import workloads as wl
+    stream = torch.cuda.current_stream()
+    if args.only == "prefill":
+        x = wl.workload_2()
+        q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
+        o = torch.empty_like(q)
+        fn = lambda: pkg.attn_prefill(q, k, v, o, scale=x.scale, stream=stream)
+        work = {"flops_per_launch": causal_flops(x.B, x.Hq, x.N, x.d)}
+    elif args.only == "decode":
+        x = wl.workload_5()
+        t = [a.to(dev) for a in (x.q, x.k_pages, x.v_pages, x.block_table, x.seq_lens)]
+        o = torch.empty_like(t[0])
+        splits = pkg.attn_decode_num_splits(x.B, x.Hkv, x.max_pages_per_seq, 0)
+        ws = torch.empty(pkg.attn_decode_workspace_size(x.B, x.Hq, x.Hkv, x.d, x.max_pages_per_seq, 0) // 4 + 4,
+                         dtype=torch.float32, device=dev)
+        fn = lambda: pkg.attn_decode(*t, o, scale=x.scale, num_splits=splits, workspace=ws, stream=stream)
+        work = {"kv_bytes_per_call": kv_bytes(x.seq_lens.tolist(), x.Hkv, x.d)}
+    else:
+        n = 1 << 29  # 2**29 bf16 = 1 GiB read + 1 GiB written per launch
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        fn = lambda: dst.copy_(src)
+        work = {"bytes_read_per_launch": 2 * n, "bytes_written_per_launch": 2 * n}
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    print(json.dumps({"only": args.only, "steps": args.steps,
+                      "avg_us": round(a.elapsed_time(b) * 1e3 / args.steps, 2), **work}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,12 +149,14 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8)
-    ap.add_argument("--skip-decode", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+                    help="launch only this kernel (for counter runs under rocprofv3); "
+                         "'copy' is a plain 1 GiB device copy used to calibrate byte counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the kernels shard over (batch, KV head) with no exchange; see DESIGN.md)",
+              "(the kernels would shard over (batch, KV head) with no exchange)",
               file=sys.stderr)
         return 2
 
@@ -124,6 +167,8 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     pkg.lib()
     dev = torch.device("cuda:0")
+    if args.only:
+        return only(args, dev)
 
     log("generating inputs ...")
     x2 = wl.workload_2()
@@ -146,9 +191,8 @@ def main() -> int:
         pkg.attn_prefill(q, k, v, o, scale=x2.scale, stream=stream)
         if evs is not None:
             evs[1].record(stream)
-        if not args.skip_decode:
-            pkg.attn_decode(dq, dk, dv, dbt, dsl, do, scale=x5.scale, num_splits=splits, workspace=ws,
-                            stream=stream)
+        pkg.attn_decode(dq, dk, dv, dbt, dsl, do, scale=x5.scale, num_splits=splits, workspace=ws,
+                        stream=stream)
         if evs is not None:
             evs[2].record(stream)
 
@@ -176,7 +220,7 @@ def main() -> int:
     flops = causal_flops(x2.B, x2.Hq, x2.N, x2.d)
     tflops = flops / (pre_avg * 1e-3) / 1e12
     kvb = kv_bytes(x5.seq_lens.tolist(), x5.Hkv, x5.d)
-    gbs = kvb / (dec_avg * 1e-3) / 1e9 if not args.skip_decode else None
+    gbs = kvb / (dec_avg * 1e-3) / 1e9
     log(f"prefill avg {pre_avg * 1e3:.1f} us ({tflops:.1f} TFLOP/s, min {min(pre_ms) * 1e3:.1f} us); "
         f"decode avg {dec_avg * 1e3:.1f} us ({gbs} GB/s); wall {t_wall:.3f} s")
 
@@ -209,7 +253,7 @@ def main() -> int:
             "traffic": traffic,
             "kernel": "prefill_bf16_kernel<128,2,4,64>", "avg_launch_us": round(pre_avg * 1e3, 2),
         },
-        "decode": None if args.skip_decode else {
+        "decode": {
             "value": round(gbs, 2), "unit": "GB/s", "avg_call_us": round(dec_avg * 1e3, 2),
             "kv_bytes_per_call": kvb,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
