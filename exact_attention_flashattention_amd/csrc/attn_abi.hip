@@ -87,7 +87,10 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o,
 
 int attn_decode_num_splits(int B, int Hkv, int max_pages_per_seq, int num_splits) {
   if (B < 1 || Hkv < 1 || max_pages_per_seq < 1 || num_splits < 0) return ATTN_ERR_SHAPE;
-  if (num_splits > 0) return num_splits < max_pages_per_seq ? num_splits : max_pages_per_seq;
+  if (num_splits > 0) {
+    int s = num_splits < max_pages_per_seq ? num_splits : max_pages_per_seq;
+    return s < 1024 ? s : 1024;  // the merge keeps one weight per split on chip
+  }
   return attn::auto_decode_splits(B, Hkv, max_pages_per_seq);
 }
 

@@ -17,11 +17,13 @@
 // rescaling the online softmax applies between tiles.
 //
 // Mapping onto CDNA4 (decode streams every cached byte once, so the design
-// goal is bytes in flight, not arithmetic):
-//  * One work-group = 4 waves = one (sequence, KV head, group of <= 16 query
-//    heads, split). Wave w of the group takes pages first+w, first+w+4, ...
-//    so the K/V of each page are read once and shared by all query heads of
-//    the GQA group.
+// goal is the memory access pattern, not arithmetic):
+//  * A "unit" is one KV head together with a group of <= 16 of its query
+//    heads. A work-group is 8 independent waves, one unit each, all on the
+//    same (sequence, split): the 8 waves walk the same pages in the same
+//    order, so each page (all KV heads of 16 tokens) is read by one CU at
+//    about the same time, as whole contiguous rows. The K/V of a page slice
+//    are read from HBM once and shared by all query heads of the unit.
 //  * Scores for a page are S^T (16 slots x 16 heads) = K q^T with
 //    v_mfma_f32_16x16x32_bf16; the K operand is loaded straight from HBM in
 //    the MFMA layout (16-byte loads). Unused head columns carry q = 0.
@@ -29,11 +31,12 @@
 //    O^T (d x heads) += V^T P^T with v_mfma_f32_16x16x16_bf16; slots past the
 //    end of the sequence are written as zeros so that a NaN left in an unused
 //    slot cannot reach the output (0 * NaN would).
-//  * The next page's K and V loads are issued before the current page is
-//    consumed (one page of prefetch per wave, 16 waves per CU).
-//  * The 4 wave partials are combined in LDS into one partial per split; the
-//    split boundaries depend only on logical page numbers, so the result is
-//    independent of where the pages sit in the pool.
+//  * Each wave keeps ATTN_DECODE_PREFETCH pages of loads in flight ahead of
+//    the page it consumes, and caches its next 64 block-table entries in one
+//    register (lane t holds entry t), so no load waits on a table lookup.
+//  * Every wave writes its own partial; the split boundaries depend only on
+//    logical page numbers, so the result is independent of where the pages
+//    sit in the pool.
 #include "attn_internal.h"
 
 namespace attn {
@@ -49,7 +52,14 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int PAGE = 16;
-constexpr int NWD = 4;  // waves per work-group
+constexpr int NWU = 8;  // waves (units) per work-group
+
+#ifndef ATTN_DECODE_WAVES_PER_SIMD
+#define ATTN_DECODE_WAVES_PER_SIMD 2
+#endif
+#ifndef ATTN_DECODE_PREFETCH
+#define ATTN_DECODE_PREFETCH 1
+#endif
 
 __device__ __forceinline__ f32x4_t mfma_16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -62,6 +72,11 @@ __device__ __forceinline__ f32x4_t mfma_16x16x16(u32x2_t a, u32x2_t b, f32x4_t c
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
   f32x2_t f = {lo, hi};
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2_t));
+}
+// lo + hi + acc for a packed pair of bf16 values (exact products with 1.0)
+__device__ __forceinline__ float add_bf16x2(unsigned pk, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk),
+                                         __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
 }
 
 // Element offset of (physical page, slot, KV head, dim 0) in a
@@ -77,26 +92,30 @@ struct DCfg {
   static constexpr int VROW = D * 2 + 16;        // bytes per slot row of a staged V page
   static constexpr int VCH = PAGE * D / 8 / 64;  // 16-byte V chunks per lane per page
   static constexpr int VPAGE = PAGE * VROW;      // bytes of one staged V page
-  static constexpr int COMB = NWD * 16 * (D + 2) * 4;  // combine area
-  static constexpr int LDS = (NWD * VPAGE > COMB) ? NWD * VPAGE : COMB;
 };
 
 template <int D>
-__global__ __launch_bounds__(NWD * 64) void decode_split_kernel(DecodeParams p, int HG) {
+__global__ __launch_bounds__(NWU * 64, ATTN_DECODE_WAVES_PER_SIMD) void decode_split_kernel(DecodeParams p, int HG) {
   using C = DCfg<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[NWU * C::VPAGE];
 
   const int S = p.num_splits;
+  const int units = p.Hkv * HG;
+  const int UG = (units + NWU - 1) / NWU;
   int w = blockIdx.x;
   const int split = w % S;
   w /= S;
-  const int hgrp = w % HG;
-  w /= HG;
-  const int kvh = w % p.Hkv;
-  const int b = w / p.Hkv;
+  const int ug = w % UG;
+  const int b = w / UG;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int unit = ug * NWU + wave;
+  if (unit >= units) return;  // no barrier below: idle waves may leave
+  const int kvh = unit / HG;
+  const int hgrp = unit - kvh * HG;
 
   const int g = p.Hq / p.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15;   // head column (B operand, S^T and O^T columns)
   const int rg = lane >> 4;  // row group: key slots rg*4..rg*4+3 of S^T, dims of O^T
   const int head_local = hgrp * 16 + j;
@@ -128,9 +147,21 @@ __global__ __launch_bounds__(NWD * 64) void decode_split_kernel(DecodeParams p, 
   float m_run = kNegInf, l_run = 0.f;
 
   unsigned char* const vst = lds + wave * C::VPAGE;
-  u32x4_t kreg[C::KS], vreg[C::VCH];
+
+  // Block-table entries of this wave's pages, 64 at a time in one VGPR (lane t
+  // holds the entry of page tbase + t), so a page's loads never wait on a
+  // dependent scalar load of its table entry.
+  int tcache = 0, tbase = -64;
+  auto phys_of = [&](int pg) {
+    if (pg - tbase >= 64) {
+      tbase = pg;
+      const int mine = pg + lane;
+      tcache = mine < pg_end ? table[mine] : 0;
+    }
+    return __builtin_amdgcn_readlane(tcache, pg - tbase);
+  };
   auto load_page = [&](int pg, u32x4_t (&kr)[C::KS], u32x4_t (&vr)[C::VCH]) {
-    const int phys = table[pg];
+    const int phys = phys_of(pg);
 #pragma unroll
     for (int s = 0; s < C::KS; ++s)
       kr[s] = *(const u32x4_t*)(kp + kv_row_offset(phys, j, kvh, p.Hkv, D) + s * 32 + rg * 8);
@@ -142,27 +173,22 @@ __global__ __launch_bounds__(NWD * 64) void decode_split_kernel(DecodeParams p, 
     }
   };
 
-  int pg = pg_begin + wave;
-  if (pg < pg_end) load_page(pg, kreg, vreg);
-  for (; pg < pg_end; pg += NWD) {
-    u32x4_t kn[C::KS], vn[C::VCH];
-    const bool more = pg + NWD < pg_end;
-    if (more) load_page(pg + NWD, kn, vn);
-
+  // consume one page whose K and V are already in registers
+  auto consume = [&](int pg, const u32x4_t (&kr)[C::KS], const u32x4_t (&vr)[C::VCH]) {
     const int valid = min(PAGE, L - pg * PAGE);  // slots of this page that hold tokens
     // stage V (zeros in unused slots)
 #pragma unroll
     for (int i = 0; i < C::VCH; ++i) {
       const int ch = lane + 64 * i;
       const int slot = ch / (D / 8), dch = ch - slot * (D / 8);
-      const u32x4_t val = slot < valid ? vreg[i] : u32x4_t{0u, 0u, 0u, 0u};
+      const u32x4_t val = slot < valid ? vr[i] : u32x4_t{0u, 0u, 0u, 0u};
       *(u32x4_t*)(vst + slot * C::VROW + dch * 16) = val;
     }
 
     // S^T = K q^T : lane holds slots rg*4 + e for head j
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) sacc = mfma_16x16x32(kreg[s], qreg[s], sacc);
+    for (int s = 0; s < C::KS; ++s) sacc = mfma_16x16x32(kr[s], qreg[s], sacc);
 
     float sv[4];
     float mx = kNegInf;
@@ -179,18 +205,10 @@ __global__ __launch_bounds__(NWD * 64) void decode_split_kernel(DecodeParams p, 
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     m_run = m_new;
     u32x2_t pb;
-    float rs;
-    {
-      const float p0 = __builtin_amdgcn_exp2f(sv[0] - m_use);
-      const float p1 = __builtin_amdgcn_exp2f(sv[1] - m_use);
-      const float p2 = __builtin_amdgcn_exp2f(sv[2] - m_use);
-      const float p3 = __builtin_amdgcn_exp2f(sv[3] - m_use);
-      pb[0] = pack_bf16x2(p0, p1);
-      pb[1] = pack_bf16x2(p2, p3);
-      rs = __builtin_bit_cast(float, pb[0] << 16) + __builtin_bit_cast(float, pb[0] & 0xffff0000u) +
-           __builtin_bit_cast(float, pb[1] << 16) + __builtin_bit_cast(float, pb[1] & 0xffff0000u);
-    }
-    l_run = l_run * alpha + rs;  // partial over this lane's 4 slots; summed over row groups at the end
+    pb[0] = pack_bf16x2(__builtin_amdgcn_exp2f(sv[0] - m_use), __builtin_amdgcn_exp2f(sv[1] - m_use));
+    pb[1] = pack_bf16x2(__builtin_amdgcn_exp2f(sv[2] - m_use), __builtin_amdgcn_exp2f(sv[3] - m_use));
+    // partial over this lane's 4 slots; summed over row groups at the end
+    l_run = add_bf16x2(pb[1], add_bf16x2(pb[0], l_run * alpha));
 
     __builtin_amdgcn_wave_barrier();
     // O^T += V^T P^T : A = V^T rows d = db*16 + j, keys rg*4 .. rg*4+3
@@ -207,79 +225,105 @@ __global__ __launch_bounds__(NWD * 64) void decode_split_kernel(DecodeParams p, 
       oacc[db] = mfma_16x16x16(a, pb, oacc[db] * alpha);
     }
     __builtin_amdgcn_wave_barrier();
+  };
 
-    if (more) {
-#pragma unroll
-      for (int s = 0; s < C::KS; ++s) kreg[s] = kn[s];
-#pragma unroll
-      for (int i = 0; i < C::VCH; ++i) vreg[i] = vn[i];
-    }
+  // Walk the split's pages with ATTN_DECODE_PREFETCH pages of loads in
+  // flight; the register buffers rotate by unrolling, so they are never
+  // indexed at run time.
+  int pg = pg_begin;
+#if ATTN_DECODE_PREFETCH == 1
+  u32x4_t ka[C::KS], va[C::VCH], kb[C::KS], vb[C::VCH];
+  if (pg < pg_end) load_page(pg, ka, va);
+  while (pg < pg_end) {
+    if (pg + 1 < pg_end) load_page(pg + 1, kb, vb);
+    consume(pg, ka, va);
+    if (++pg >= pg_end) break;
+    if (pg + 1 < pg_end) load_page(pg + 1, ka, va);
+    consume(pg, kb, vb);
+    ++pg;
   }
+#else
+  u32x4_t ka[C::KS], va[C::VCH], kb[C::KS], vb[C::VCH], kc[C::KS], vc[C::VCH];
+  if (pg < pg_end) load_page(pg, ka, va);
+  if (pg + 1 < pg_end) load_page(pg + 1, kb, vb);
+  while (pg < pg_end) {
+    if (pg + 2 < pg_end) load_page(pg + 2, kc, vc);
+    consume(pg, ka, va);
+    if (++pg >= pg_end) break;
+    if (pg + 2 < pg_end) load_page(pg + 2, ka, va);
+    consume(pg, kb, vb);
+    if (++pg >= pg_end) break;
+    if (pg + 2 < pg_end) load_page(pg + 2, kb, vb);
+    consume(pg, kc, vc);
+    ++pg;
+  }
+#endif
 
   // the row groups each summed 4 of the 16 slots of every page
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
 
-  // ---- combine the NWD wave partials of this split ---------------------------------
-  __syncthreads();  // every wave is done with its V staging area
-  float* comb = (float*)lds;                 // [NWD][16][D] unnormalised outputs
-  float* comb_ml = comb + NWD * 16 * D;      // [NWD][16][2]
+  // ---- this wave's partial for (b, head, split) ------------------------------------
+  if (head_ok) {
+    const long long slot = ((long long)b * p.Hq + h) * S + split;
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) comb[(wave * 16 + j) * D + db * 16 + rg * 4 + e] = oacc[db][e];
-  if (rg == 0) {
-    comb_ml[(wave * 16 + j) * 2 + 0] = m_run;
-    comb_ml[(wave * 16 + j) * 2 + 1] = l_run;
-  }
-  __syncthreads();
-
-  const int nheads = min(16, g - hgrp * 16);
-  for (int idx = tid; idx < nheads * D; idx += NWD * 64) {
-    const int hj = idx / D, d = idx - hj * D;
-    float M = kNegInf;
-#pragma unroll
-    for (int wv = 0; wv < NWD; ++wv) M = fmaxf(M, comb_ml[(wv * 16 + hj) * 2]);
-    const float M_use = (M == kNegInf) ? 0.f : M;
-    float acc = 0.f, lsum = 0.f;
-#pragma unroll
-    for (int wv = 0; wv < NWD; ++wv) {
-      const float sc = __builtin_amdgcn_exp2f(comb_ml[(wv * 16 + hj) * 2] - M_use);
-      acc += sc * comb[(wv * 16 + hj) * D + d];
-      lsum += sc * comb_ml[(wv * 16 + hj) * 2 + 1];
-    }
-    const int hh = kvh * g + hgrp * 16 + hj;
-    const long long slot = ((long long)b * p.Hq + hh) * S + split;
-    p.ws_o[slot * D + d] = acc;
-    if (d == 0) {
-      p.ws_ml[slot * 2 + 0] = M;
-      p.ws_ml[slot * 2 + 1] = lsum;
+    for (int db = 0; db < C::DB; ++db)
+      *(f32x4_t*)(p.ws_o + slot * D + db * 16 + rg * 4) = oacc[db];
+    if (rg == 0) {
+      p.ws_ml[slot * 2 + 0] = m_run;
+      p.ws_ml[slot * 2 + 1] = l_run;
     }
   }
 }
 
 // Merge the split partials of one (sequence, query head): M = max_s m_s,
 // o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s; zero when no split saw a key.
+// One wave per (sequence, head): the split weights are computed once, in
+// parallel across lanes, then every lane sums D/64 output dims over the splits
+// in a fixed order.
+constexpr int MERGE_MAX_SPLITS = 1024;
 template <int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
+  __shared__ float wts[MERGE_MAX_SPLITS];
   const int bh = blockIdx.x;
-  const int d = threadIdx.x;
+  const int lane = threadIdx.x;
   const int S = p.num_splits;
   const float* ml = p.ws_ml + (long long)bh * S * 2;
   const float* po = p.ws_o + (long long)bh * S * D;
   float M = kNegInf;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
-  float out = 0.f;
-  if (M != kNegInf) {
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float sc = __builtin_amdgcn_exp2f(ml[2 * s] - M);
-      num += sc * po[(long long)s * D + d];
-      den += sc * ml[2 * s + 1];
-    }
-    out = num / den;
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, ml[2 * s]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  float den = 0.f;
+  for (int s = lane; s < S; s += 64) {
+    const float w = (M == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ml[2 * s] - M);
+    wts[s] = w;
+    den += w * ml[2 * s + 1];
   }
-  ((__bf16*)p.o)[(long long)bh * D + d] = (__bf16)out;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
+  __syncthreads();
+  constexpr int PER = D / 64;  // output dims per lane
+  float num[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) num[i] = 0.f;
+  int s = 0;
+  for (; s + 4 <= S; s += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float w = wts[s + u];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) num[i] += w * po[(long long)(s + u) * D + i * 64 + lane];
+    }
+  }
+  for (; s < S; ++s) {
+    const float w = wts[s];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) num[i] += w * po[(long long)s * D + i * 64 + lane];
+  }
+  const float inv = (den > 0.f) ? 1.f / den : 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) ((__bf16*)p.o)[(long long)bh * D + i * 64 + lane] = (__bf16)(num[i] * inv);
 }
 
 // Copy token rows out of the page pool through the block table (test aid).
@@ -302,21 +346,23 @@ template <int D>
 hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
   const int g = p.Hq / p.Hkv;
   const int HG = (g + 15) / 16;
-  const long long total = (long long)p.B * p.Hkv * HG * p.num_splits;
+  const long long units = (long long)p.Hkv * HG;
+  const long long total = (long long)p.B * ((units + NWU - 1) / NWU) * p.num_splits;
   if (total <= 0 || total > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)total), dim3(NWD * 64), 0, stream, p, HG);
+  hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)total), dim3(NWU * 64), 0, stream, p, HG);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)(p.B * p.Hq)), dim3(D), 0, stream, p);
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)(p.B * p.Hq)), dim3(64), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 int auto_decode_splits(int B, int Hkv, int max_pages_per_seq) {
+  // aim for about 4096 (sequence, KV head, split) waves, at least 16 pages each
   const long long pairs = (long long)B * Hkv;
-  long long s = (1024 + pairs - 1) / pairs;
-  const long long cap = max(1, max_pages_per_seq / 8);
+  long long s = (4096 + pairs - 1) / pairs;
+  const long long cap = max(1, max_pages_per_seq / 16);
   if (s > cap) s = cap;
   if (s < 1) s = 1;
   return (int)s;

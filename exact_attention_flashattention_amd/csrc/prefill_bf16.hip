@@ -208,19 +208,39 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
 
   // ---- global -> register staging of one K/V tile ----------------------------
   u32x4_t kst[C::CPT][C::KPC], vst[C::CPT][C::KPC];
+  // this thread's chunk offsets within a tile (element units), computed once
+  long long st_off[C::CPT];
+#pragma unroll
+  for (int i = 0; i < C::CPT; ++i) {
+    const int ch = tid + i * C::NT;
+    const int kgrp = ch / (D / 8), dch = ch - kgrp * (D / 8);
+    st_off[i] = (long long)(kgrp * C::KPC) * p.k_sn + dch * 8;
+  }
   auto load_tile = [&](int k0) {
+    const long long tile_off = (long long)k0 * p.k_sn;  // scalar
+    const bool tail = k0 + BN > N;
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int ch = tid + i * C::NT;
       if (C::CHUNKS < C::NT && ch >= C::CHUNKS) break;  // whole waves idle here
-      const int kgrp = ch / (D / 8), dch = ch - kgrp * (D / 8);
+      if (!tail) {
+        const __bf16* kp = kg + tile_off + st_off[i];
+        const __bf16* vp = vg + tile_off + st_off[i];
 #pragma unroll
-      for (int r = 0; r < C::KPC; ++r) {
-        // rows past the end are clamped here and zero-filled by store_tile
-        const int key = min(k0 + kgrp * C::KPC + r, N - 1);
-        const long long off = (long long)key * p.k_sn + dch * 8;
-        kst[i][r] = *(const u32x4_t*)(kg + off);
-        vst[i][r] = *(const u32x4_t*)(vg + off);
+        for (int r = 0; r < C::KPC; ++r) {
+          kst[i][r] = *(const u32x4_t*)(kp + r * p.k_sn);
+          vst[i][r] = *(const u32x4_t*)(vp + r * p.k_sn);
+        }
+      } else {
+        const int kgrp = ch / (D / 8), dch = ch - kgrp * (D / 8);
+#pragma unroll
+        for (int r = 0; r < C::KPC; ++r) {
+          // rows past the end are clamped here and zero-filled by store_tile
+          const int key = min(k0 + kgrp * C::KPC + r, N - 1);
+          const long long off = (long long)key * p.k_sn + dch * 8;
+          kst[i][r] = *(const u32x4_t*)(kg + off);
+          vst[i][r] = *(const u32x4_t*)(vg + off);
+        }
       }
     }
   };
@@ -291,13 +311,15 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   auto prep = [&](int t, f32x16_t (&s)[C::KB]) {
     const int k0 = t * BN;
     if ((p.causal && k0 + BN - 1 > qw0) || (k0 + BN > N)) {
+      // key k0 + h2*4 + off (off a compile-time constant per element) is visible
+      // iff off <= lim
+      const int lim = (p.causal ? min(qi, N - 1) : N - 1) - k0 - h2 * 4;
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int key = k0 + kb * 32 + (e >> 2) * 8 + h2 * 4 + (e & 3);
-          const bool dead = key >= N || (p.causal && key > qi);
-          s[kb][e] = dead ? kNegInf : s[kb][e];
+          const int off = kb * 32 + (e >> 2) * 8 + (e & 3);
+          s[kb][e] = (off > lim) ? kNegInf : s[kb][e];
         }
     }
     float mr = kNegInf;

@@ -116,7 +116,7 @@ int attn_prefill_ex(const void* q, const void* k, const void* v, void* o, float*
 /*
  * attn_decode_num_splits - the number of context splits attn_decode uses.
  *
- * num_splits > 0 is returned unchanged (clamped to max_pages_per_seq); 0 asks
+ * num_splits > 0 is returned clamped to [1, min(max_pages_per_seq, 1024)]; 0 asks
  * for the automatic choice, which depends only on the arguments given here
  * (not on the device), so that a result can be reproduced exactly. Returns
  * a negative status for invalid sizes.

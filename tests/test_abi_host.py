@@ -108,7 +108,7 @@ def test_split_count_and_workspace_size(L):
     assert L.attn_decode_num_splits(4, 8, 100, 7) == 7
     assert L.attn_decode_num_splits(4, 8, 5, 7) == 5
     auto = L.attn_decode_num_splits(4, 8, 8192, 0)
-    assert 1 <= auto <= 8192 // 8
+    assert 1 <= auto <= 8192 // 16
     assert L.attn_decode_num_splits(64, 8, 512, 0) >= 1
     assert L.attn_decode_num_splits(0, 8, 512, 0) == ERR["ATTN_ERR_SHAPE"]
     assert L.attn_decode_workspace_size(4, 64, 8, 128, 8192, 0) == 4 * 64 * auto * 130 * 4
