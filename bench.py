@@ -68,7 +68,7 @@ def measured_traffic(kernel: str, sources) -> float | None:
     return float(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
 
 
-def cpu_baseline(x2, x5, heads: int):
+def cpu_baseline(x2, x5, batches: int):
     """Time the oracle (unchanged) on a bounded sample of both workloads."""
     import numpy as np
     from oracle import attention_oracle as ao
@@ -77,28 +77,83 @@ def cpu_baseline(x2, x5, heads: int):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
-    g = x2.Hq // x2.Hkv
-    hs = max(g, heads - heads % g)
-    q = ao.to_bhnd(x2.q[:1, :, :hs], "BNHD")
-    k = ao.to_bhnd(x2.k[:1, :, :hs // g], "BNHD")
-    v = ao.to_bhnd(x2.v[:1, :, :hs // g], "BNHD")
+    nb = max(1, min(x2.B, batches))
+    q = ao.to_bhnd(x2.q[:nb], "BNHD")
+    k = ao.to_bhnd(x2.k[:nb], "BNHD")
+    v = ao.to_bhnd(x2.v[:nb], "BNHD")
     t0 = time.perf_counter()
     ao.sdpa_ref(q, k, v, x2.scale, causal=True)
     tp = time.perf_counter() - t0
-    pf = causal_flops(1, hs, x2.N, x2.d) / tp / 1e12
-    sel = [0]
+    pflops = causal_flops(nb, x2.Hq, x2.N, x2.d)
+    pf = pflops / tp / 1e12
     t0 = time.perf_counter()
-    ao.decode_ref(x5.q[sel], x5.k_pages, x5.v_pages, x5.block_table[sel], x5.seq_lens[sel], x5.scale)
+    ao.decode_ref(x5.q, x5.k_pages, x5.v_pages, x5.block_table, x5.seq_lens, x5.scale)
     td = time.perf_counter() - t0
-    dg = kv_bytes(x5.seq_lens[sel].tolist(), x5.Hkv, x5.d) / td / 1e9
+    dg = kv_bytes(x5.seq_lens.tolist(), x5.Hkv, x5.d) / td / 1e9
     return {
         "value": round(pf, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-        "sample": f"prefill: batch 0, query heads 0..{hs - 1} of the headline prefill (full N={x2.N}, "
-                  f"causal-FLOP count {causal_flops(1, hs, x2.N, x2.d)}) in {tp:.2f} s; "
-                  f"decode: sequence 0 of the paged decode (L={int(x5.seq_lens[0])}) in {td:.2f} s",
+        "sample": f"prefill: batch entries 0..{nb - 1} (all {x2.Hq} query heads, full N={x2.N}) of the "
+                  f"headline prefill, causal-FLOP count {pflops}, in {tp:.2f} s; decode: all {x5.B} "
+                  f"sequences of the paged decode ({kv_bytes(x5.seq_lens.tolist(), x5.Hkv, x5.d)} KV bytes) "
+                  f"in {td:.2f} s",
         "decode_value": round(dg, 4), "decode_unit": "GB/s",
         "blas": "OpenBLAS (numpy)",
     }
+
+
+PREFILL_SOURCES = ["prefill_bf16.hip", "attn_internal.h"]
+DECODE_SOURCES = ["decode.hip", "attn_internal.h"]
+
+
+def write_traffic(root: str) -> int:
+    """Turn rocprofv3 --pmc CSVs into profiles/traffic.json (no GPU needed).
+
+    Expects <root>/<COUNTER>_<kind>/**/*counter_collection.csv for COUNTER in
+    FETCH_SIZE, WRITE_SIZE and kind in prefill, decode, copy, as written by
+        rocprofv3 --pmc <COUNTER> -d <root>/<COUNTER>_<kind> -o run --output-format csv \
+            -- python bench.py --only <kind> --steps 3 --warmup 1 > <root>/<COUNTER>_<kind>.log
+    Each counter (KiB per dispatch) is scaled by the ratio between the bytes a
+    plain 1 GiB device copy moves and what the same counter reports for it.
+    The kernel source hash each run printed into its .log must match the
+    current source, else nothing is written.
+    """
+    import csv
+    import glob
+
+    def per_dispatch(counter, kind, name_part):
+        vals = []
+        for f in glob.glob(os.path.join(root, f"{counter}_{kind}", "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+                    vals.append(float(r["Counter_Value"]) * 1024.0)
+        if not vals:
+            raise SystemExit(f"no {counter} rows for {name_part} under {root}")
+        return sum(vals) / len(vals)
+
+    copy_bytes = float(1 << 30)
+    fetch_factor = copy_bytes / per_dispatch("FETCH_SIZE", "copy", "copyBuffer")
+    write_factor = copy_bytes / per_dispatch("WRITE_SIZE", "copy", "copyBuffer")
+    out = {"calibration": {"copy_bytes_each_way": copy_bytes, "fetch_factor": round(fetch_factor, 4),
+                           "write_factor": round(write_factor, 4)}}
+    for key, kind, parts, srcs in [("prefill_bf16", "prefill", ["prefill_bf16_kernel"], PREFILL_SOURCES),
+                                   ("decode", "decode", ["decode_split_kernel", "decode_merge_kernel"],
+                                    DECODE_SOURCES)]:
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            ran = None
+            with open(os.path.join(root, f"{counter}_{kind}.log")) as f:
+                for line in f:
+                    if line.startswith('{"only"'):
+                        ran = json.loads(line).get("source_sha256")
+            if ran != source_hash(*srcs):
+                raise SystemExit(f"{counter}_{kind}: counters were taken from another kernel source")
+        fetch = sum(per_dispatch("FETCH_SIZE", kind, n) for n in parts) * fetch_factor
+        write = sum(per_dispatch("WRITE_SIZE", kind, n) for n in parts) * write_factor
+        out[key] = {"source_sha256": source_hash(*srcs), "kernels": parts,
+                    "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write)}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+    return 0
 
 
 def only(args, dev) -> int:
@@ -137,8 +192,10 @@ def only(args, dev) -> int:
         fn()
     b.record(stream)
     torch.cuda.synchronize()
+    srcs = {"prefill": PREFILL_SOURCES, "decode": DECODE_SOURCES}.get(args.only)
     print(json.dumps({"only": args.only, "steps": args.steps,
-                      "avg_us": round(a.elapsed_time(b) * 1e3 / args.steps, 2), **work}), flush=True)
+                      "avg_us": round(a.elapsed_time(b) * 1e3 / args.steps, 2),
+                      "source_sha256": source_hash(*srcs) if srcs else None, **work}), flush=True)
     return 0
 
 
@@ -148,11 +205,16 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--cpu-batches", type=int, default=2,
+                    help="batch entries of the headline prefill the CPU oracle is timed on")
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
                     help="launch only this kernel (for counter runs under rocprofv3); "
                          "'copy' is a plain 1 GiB device copy used to calibrate byte counters")
+    ap.add_argument("--write-traffic", metavar="DIR", default=None,
+                    help="parse rocprofv3 FETCH_SIZE/WRITE_SIZE runs under DIR into profiles/traffic.json")
     args = ap.parse_args()
+    if args.write_traffic:
+        return write_traffic(args.write_traffic)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -224,8 +286,8 @@ def main() -> int:
     log(f"prefill avg {pre_avg * 1e3:.1f} us ({tflops:.1f} TFLOP/s, min {min(pre_ms) * 1e3:.1f} us); "
         f"decode avg {dec_avg * 1e3:.1f} us ({gbs} GB/s); wall {t_wall:.3f} s")
 
-    traffic = measured_traffic("prefill_bf16", ["prefill_bf16.hip", "attn_internal.h"])
-    dtraffic = measured_traffic("decode", ["decode.hip", "attn_internal.h"])
+    traffic = measured_traffic("prefill_bf16", PREFILL_SOURCES)
+    dtraffic = measured_traffic("decode", DECODE_SOURCES)
     result = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -251,7 +313,7 @@ def main() -> int:
             "bound": "mfma", "achieved": round(tflops, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "prefill_bf16_kernel<128,2,4,64>", "avg_launch_us": round(pre_avg * 1e3, 2),
+            "kernel": "prefill_bf16_kernel<128,8,64>", "avg_launch_us": round(pre_avg * 1e3, 2),
         },
         "decode": {
             "value": round(gbs, 2), "unit": "GB/s", "avg_call_us": round(dec_avg * 1e3, 2),
@@ -264,7 +326,7 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
-        result["cpu_baseline"] = cpu_baseline(x2, x5, args.cpu_heads)
+        result["cpu_baseline"] = cpu_baseline(x2, x5, args.cpu_batches)
     print(json.dumps(result), flush=True)
     return 0
 

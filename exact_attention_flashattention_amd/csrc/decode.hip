@@ -278,52 +278,68 @@ __global__ __launch_bounds__(NWU * 64, ATTN_DECODE_WAVES_PER_SIMD) void decode_s
 
 // Merge the split partials of one (sequence, query head): M = max_s m_s,
 // o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s; zero when no split saw a key.
-// One wave per (sequence, head): the split weights are computed once, in
-// parallel across lanes, then every lane sums D/64 output dims over the splits
-// in a fixed order.
+// One 256-thread work-group per (sequence, head): the split weights are
+// computed once, in parallel; then 256/D groups of D threads each sum every
+// (256/D)-th split for one output dim, and the group sums are added in a fixed
+// order (so the result does not depend on timing).
 constexpr int MERGE_MAX_SPLITS = 1024;
+constexpr int MERGE_THREADS = 256;
 template <int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
+__global__ __launch_bounds__(MERGE_THREADS) void decode_merge_kernel(DecodeParams p) {
+  constexpr int G = MERGE_THREADS / D;  // split groups
   __shared__ float wts[MERGE_MAX_SPLITS];
+  __shared__ float red[MERGE_THREADS / 64];
+  __shared__ float part[G][D];
   const int bh = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int S = p.num_splits;
   const float* ml = p.ws_ml + (long long)bh * S * 2;
   const float* po = p.ws_o + (long long)bh * S * D;
+
   float M = kNegInf;
-  for (int s = lane; s < S; s += 64) M = fmaxf(M, ml[2 * s]);
+  for (int s = tid; s < S; s += MERGE_THREADS) M = fmaxf(M, ml[2 * s]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if (lane == 0) red[wv] = M;
+  __syncthreads();
+  M = red[0];
+#pragma unroll
+  for (int i = 1; i < MERGE_THREADS / 64; ++i) M = fmaxf(M, red[i]);
+  __syncthreads();
+
   float den = 0.f;
-  for (int s = lane; s < S; s += 64) {
+  for (int s = tid; s < S; s += MERGE_THREADS) {
     const float w = (M == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ml[2 * s] - M);
     wts[s] = w;
     den += w * ml[2 * s + 1];
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
+  if (lane == 0) red[wv] = den;
   __syncthreads();
-  constexpr int PER = D / 64;  // output dims per lane
-  float num[PER];
+  den = 0.f;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) num[i] = 0.f;
-  int s = 0;
-  for (; s + 4 <= S; s += 4) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float w = wts[s + u];
-#pragma unroll
-      for (int i = 0; i < PER; ++i) num[i] += w * po[(long long)(s + u) * D + i * 64 + lane];
-    }
+  for (int i = 0; i < MERGE_THREADS / 64; ++i) den += red[i];
+
+  const int d = tid % D, grp = tid / D;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  int s = grp;
+  for (; s + 3 * G < S; s += 4 * G) {
+    a0 += wts[s] * po[(long long)s * D + d];
+    a1 += wts[s + G] * po[(long long)(s + G) * D + d];
+    a2 += wts[s + 2 * G] * po[(long long)(s + 2 * G) * D + d];
+    a3 += wts[s + 3 * G] * po[(long long)(s + 3 * G) * D + d];
   }
-  for (; s < S; ++s) {
-    const float w = wts[s];
+  for (; s < S; s += G) a0 += wts[s] * po[(long long)s * D + d];
+  part[grp][d] = (a0 + a1) + (a2 + a3);
+  __syncthreads();
+  if (grp == 0) {
+    float num = part[0][d];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) num[i] += w * po[(long long)s * D + i * 64 + lane];
+    for (int i = 1; i < G; ++i) num += part[i][d];
+    const float inv = (den > 0.f) ? 1.f / den : 0.f;
+    ((__bf16*)p.o)[(long long)bh * D + d] = (__bf16)(num * inv);
   }
-  const float inv = (den > 0.f) ? 1.f / den : 0.f;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) ((__bf16*)p.o)[(long long)bh * D + i * 64 + lane] = (__bf16)(num[i] * inv);
 }
 
 // Copy token rows out of the page pool through the block table (test aid).
@@ -352,7 +368,7 @@ hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)total), dim3(NWU * 64), 0, stream, p, HG);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)(p.B * p.Hq)), dim3(64), 0, stream, p);
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)(p.B * p.Hq)), dim3(MERGE_THREADS), 0, stream, p);
   return hipGetLastError();
 }
 
