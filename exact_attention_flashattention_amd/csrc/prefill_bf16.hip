@@ -20,17 +20,21 @@
 //    in-lane reductions plus one v_permlane32_swap between the lane halves.
 //  * The same lane layout is exactly the B operand of O^T += V^T P^T (after
 //    rounding P to bf16) provided the 16 keys of each MFMA k-step are taken in
-//    the order the S^T accumulator hands them out. V is therefore written to
-//    LDS transposed ([d][key]) in that order, so each A-operand read of V^T is
-//    one 16-byte LDS load. The 16-byte granules of a V^T row are XOR-swizzled
-//    by row so that neither the transposing writes nor the operand reads
-//    collide on LDS banks.
+//    the order the S^T accumulator hands them out. V stays in its natural
+//    [key][d] layout in LDS; the V^T operand is read with ds_read_b64_tr_b16,
+//    whose 16-lane transpose hands each lane four consecutive keys of one
+//    dimension, so two such reads form one A operand in exactly that key order.
+//  * K and V tiles are copied HBM -> LDS with global_load_lds_dwordx4 (no
+//    registers, no LDS store instructions). Each 16-byte chunk of a row is
+//    stored at a position XOR-swizzled by the row, chosen so that both the K
+//    operand reads (16 consecutive rows, one chunk each) and the transposed V
+//    reads (4 consecutive rows, two chunks each) hit distinct LDS banks.
 //  * Software pipeline: while tile j's scores are exponentiated and multiplied
 //    into V (vector ALU + MFMA), the MFMAs of tile j+1's scores are already in
 //    flight, all in one basic block, so the matrix cores and the vector ALU
-//    work at the same time. Three LDS buffers rotate: tile j (V read), tile
-//    j+1 (K read) and tile j+2 (being written from registers loaded earlier in
-//    the same iteration); one barrier per tile.
+//    work at the same time. Four LDS buffers rotate: tile j (V read), tile
+//    j+1 (K read), tile j+2 (landed) and tile j+3 (loads in flight, issued
+//    three iterations before use); one barrier per tile.
 //  * The reference point m used in 2^(s - m) is only moved when a row's max
 //    exceeds it by more than 2^8 (then O and l are rescaled exactly); between
 //    moves the weights are bounded by 2^8, which bf16 and fp32 represent with
@@ -42,9 +46,9 @@
 //  * Work-groups are numbered so that each XCD receives whole (b, KV head)
 //    groups (its L2 then holds those K/V), and within a group the heaviest
 //    causal query tiles start first.
-//  * Inputs must be finite: rows past the end of the sequence are zero-filled
-//    in LDS and masked, but a NaN in a visible key or value propagates, as it
-//    does in the definition.
+//  * Inputs must be finite: rows past the end of the sequence are filled with
+//    the last row (finite) and masked out of the softmax, so their weight is
+//    exactly 0.
 #include "attn_internal.h"
 
 namespace attn {
@@ -96,48 +100,54 @@ template <int D, int NW, int BN>
 struct Cfg {
   static constexpr int NT = NW * 64;
   static constexpr int BM = NW * 32;
-  static constexpr int KS = D / 16;             // k-steps of S^T = K Q^T
-  static constexpr int KB = BN / 32;            // 32-key blocks per tile
-  static constexpr int PS = BN / 16;            // 16-key k-steps of O^T += V^T P^T
-  static constexpr int DB = D / 32;             // 32-row blocks of O^T
-  static constexpr int K_STRIDE = D * 2 + 16;   // bytes per key row of K in LDS
-  static constexpr int V_STRIDE = BN * 2;       // bytes per dim row of V^T in LDS
-  static constexpr int GR = BN / 8;             // 16-byte granules per V^T row
-  static constexpr int K_BYTES = BN * K_STRIDE;
-  static constexpr int V_BYTES = D * V_STRIDE;
-  static constexpr int STAGE = K_BYTES + V_BYTES;  // one LDS buffer
-  static constexpr int NBUF = 3;
-  // Staging: a chunk is KPC consecutive keys x 8 dims; one thread moves up to
-  // CPT chunks (when there are fewer chunks than threads, the surplus waves
-  // stage nothing).
-  static constexpr int KPC = ((BN / 4) * (D / 8) >= NT) ? 4 : 2;
-  static constexpr int CHUNKS = (BN / KPC) * (D / 8);
-  static constexpr int CPT = (CHUNKS + NT - 1) / NT;
-  static_assert(CHUNKS % NT == 0 || (NT % CHUNKS == 0 && CHUNKS % 64 == 0), "uneven staging");
-  static_assert(BN % 32 == 0 && D % 32 == 0 && GR >= 4, "bad tile");
+  static constexpr int KS = D / 16;        // k-steps of S^T = K Q^T
+  static constexpr int KB = BN / 32;       // 32-key blocks per tile
+  static constexpr int PS = BN / 16;       // 16-key k-steps of O^T += V^T P^T
+  static constexpr int DB = D / 32;        // 32-row blocks of O^T
+  static constexpr int ROWB = D * 2;       // bytes per key row (K and V alike)
+  static constexpr int CPR = D / 8;        // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;     // rows per wave load instruction (1 KiB)
+  static constexpr int LPT = BN / RPI;     // load instructions per tensor per tile
+  static constexpr int IPW = (LPT + NW - 1) / NW;  // of which one wave issues at most
+  static constexpr int TILE = BN * ROWB;   // bytes of one K (or V) tile
+  static constexpr int STAGE = 2 * TILE;   // one LDS buffer: K tile then V tile
+  static constexpr int NBUF = 4;
+  static constexpr int OROW = D * 2 + 16;  // padded bytes per staged output row
+  static constexpr int LDS_BYTES = (NBUF * STAGE > NW * 32 * OROW) ? NBUF * STAGE : NW * 32 * OROW;
+  static_assert(LPT % NW == 0 || NW % LPT == 0, "uneven tile loads");
+  static_assert(BN % 32 == 0 && (D == 64 || D == 128), "bad tile");
 };
 
-// Position of tile-local key kt inside a V^T row: within every 16-key group
-// the 4-key quads are stored in the order 0, 2, 1, 3, which is the order in
-// which the S^T accumulator hands keys to the P operand (lane half 0 holds keys
-// 0-3 and 8-11 of the group, lane half 1 holds keys 4-7 and 12-15).
-__device__ __forceinline__ int vt_pos(int kt) {
-  const int quad = (kt >> 2) & 3;
-  const int pq = (quad == 1) ? 2 : (quad == 2) ? 1 : quad;
-  return (kt & ~15) | (pq << 2) | (kt & 3);
+// Physical 16-byte chunk position of logical chunk c in row r is c ^ swz(r).
+// For 16 chunks per row swz is a bijection on every 16 consecutive rows (K
+// reads: 16 lanes, 16 rows, one chunk) and maps 4 consecutive rows to values
+// differing in bits 2-3 (transposed V reads: 4 rows x 2 adjacent chunks).
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CPR == 16)
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  else
+    return ((r & 3) << 1) | ((r >> 2) & 1);
 }
 
-// Byte offset of (row r, key position pos) in the swizzled V^T buffer.
-template <int GR, int V_STRIDE>
-__device__ __forceinline__ int vt_off(int r, int pos) {
-  const int swz = ((r & 7) ^ ((r >> 3) & 7)) & (GR - 1);
-  return r * V_STRIDE + ((((pos >> 3) ^ swz)) << 4) + (pos & 7) * 2;
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void load_to_lds(const void* g, unsigned char* l) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding)
+template <int NCNT>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(NCNT >= 0 && NCNT < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((NCNT & 15) | ((NCNT >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 template <int D, int NW, int BN>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams p, int n_qtiles) {
   using C = Cfg<D, NW, BN>;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[C::NBUF * C::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS_BYTES];
 
   // ---- work decomposition --------------------------------------------------
   const int g = p.Hq / p.Hkv;
@@ -168,7 +178,11 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
 
   const int N = p.N;
   const int q_tile0 = qtile * C::BM;
-  const int qw0 = q_tile0 + wave * 32;  // first query row of this wave
+  // Query block of this wave. Waves w and w + 4 share a SIMD; pairing block w
+  // with block NW - 1 - (w - 4) gives every SIMD one early and one late block,
+  // so the causal work per SIMD is balanced.
+  const int qblk = (NW == 8 && wave >= 4) ? 11 - wave : wave;
+  const int qw0 = q_tile0 + qblk * 32;  // first query row of this wave
   const int qi = qw0 + c;               // this lane's query row
 
   const __bf16* __restrict__ qg = (const __bf16*)p.q + b * p.q_sb + h * p.q_sh;
@@ -206,94 +220,34 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   // tiles 0 .. wave_tiles-1 hold keys visible to some row of this wave
   const int wave_tiles = (qw0 >= N) ? 0 : (p.causal ? min(n_tiles, (qw0 + 31) / BN + 1) : n_tiles);
 
-  // ---- global -> register staging of one K/V tile ----------------------------
-  u32x4_t kst[C::CPT][C::KPC], vst[C::CPT][C::KPC];
-  // this thread's chunk offsets within a tile (element units), computed once
-  long long st_off[C::CPT];
-#pragma unroll
-  for (int i = 0; i < C::CPT; ++i) {
-    const int ch = tid + i * C::NT;
-    const int kgrp = ch / (D / 8), dch = ch - kgrp * (D / 8);
-    st_off[i] = (long long)(kgrp * C::KPC) * p.k_sn + dch * 8;
-  }
-  auto load_tile = [&](int k0) {
-    const long long tile_off = (long long)k0 * p.k_sn;  // scalar
-    const bool tail = k0 + BN > N;
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int ch = tid + i * C::NT;
-      if (C::CHUNKS < C::NT && ch >= C::CHUNKS) break;  // whole waves idle here
-      if (!tail) {
-        const __bf16* kp = kg + tile_off + st_off[i];
-        const __bf16* vp = vg + tile_off + st_off[i];
-#pragma unroll
-        for (int r = 0; r < C::KPC; ++r) {
-          kst[i][r] = *(const u32x4_t*)(kp + r * p.k_sn);
-          vst[i][r] = *(const u32x4_t*)(vp + r * p.k_sn);
-        }
-      } else {
-        const int kgrp = ch / (D / 8), dch = ch - kgrp * (D / 8);
-#pragma unroll
-        for (int r = 0; r < C::KPC; ++r) {
-          // rows past the end are clamped here and zero-filled by store_tile
-          const int key = min(k0 + kgrp * C::KPC + r, N - 1);
-          const long long off = (long long)key * p.k_sn + dch * 8;
-          kst[i][r] = *(const u32x4_t*)(kg + off);
-          vst[i][r] = *(const u32x4_t*)(vg + off);
-        }
-      }
-    }
-  };
+  // ---- HBM -> LDS copies of K/V tiles ----------------------------------------------
   auto buf_of = [&](int t) { return lds + (t % C::NBUF) * C::STAGE; };
-  auto store_tile = [&](int t) {
+  // this lane's part of a load instruction: tile-local row and logical chunk
+  const int ld_row = lane / C::CPR;
+  const int ld_pos = lane % C::CPR;
+  // issue the copies of tile t (this wave's share: instructions wave, wave+NW, ...)
+  auto issue_tile = [&](int t, unsigned char* __restrict__ kl) {
     const int k0 = t * BN;
-    unsigned char* const k_lds = buf_of(t);
-    unsigned char* const vt_lds = k_lds + C::K_BYTES;
-    const bool tail = k0 + BN > N;
+    unsigned char* const vl = kl + C::TILE;
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int ch = tid + i * C::NT;
-      if (C::CHUNKS < C::NT && ch >= C::CHUNKS) break;
-      const int kgrp = ch / (D / 8), dch = ch - kgrp * (D / 8);
-      const int kt0 = kgrp * C::KPC;
-      if (tail) {
-#pragma unroll
-        for (int r = 0; r < C::KPC; ++r) {
-          const bool dead = k0 + kt0 + r >= N;
-          kst[i][r] = dead ? u32x4_t{0u, 0u, 0u, 0u} : kst[i][r];
-          vst[i][r] = dead ? u32x4_t{0u, 0u, 0u, 0u} : vst[i][r];
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < C::KPC; ++r)
-        *(u32x4_t*)(k_lds + (kt0 + r) * C::K_STRIDE + dch * 16) = kst[i][r];
-      // transpose KPC keys x 8 dims into 8 rows of KPC keys
-      const int pos = vt_pos(kt0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r0 = dch * 8 + 2 * e;
-        if constexpr (C::KPC == 4) {
-          u32x2_t lo, hi;
-          lo[0] = __builtin_amdgcn_perm(vst[i][1][e], vst[i][0][e], 0x05040100u);
-          lo[1] = __builtin_amdgcn_perm(vst[i][3][e], vst[i][2][e], 0x05040100u);
-          hi[0] = __builtin_amdgcn_perm(vst[i][1][e], vst[i][0][e], 0x07060302u);
-          hi[1] = __builtin_amdgcn_perm(vst[i][3][e], vst[i][2][e], 0x07060302u);
-          *(u32x2_t*)(vt_lds + vt_off<C::GR, C::V_STRIDE>(r0, pos)) = lo;
-          *(u32x2_t*)(vt_lds + vt_off<C::GR, C::V_STRIDE>(r0 + 1, pos)) = hi;
-        } else {
-          const unsigned lo = __builtin_amdgcn_perm(vst[i][1][e], vst[i][0][e], 0x05040100u);
-          const unsigned hi = __builtin_amdgcn_perm(vst[i][1][e], vst[i][0][e], 0x07060302u);
-          *(unsigned*)(vt_lds + vt_off<C::GR, C::V_STRIDE>(r0, pos)) = lo;
-          *(unsigned*)(vt_lds + vt_off<C::GR, C::V_STRIDE>(r0 + 1, pos)) = hi;
-        }
-      }
+    for (int u = 0; u < C::IPW; ++u) {
+      const int i = wave + u * NW;
+      if (C::LPT < NW && i >= C::LPT) break;  // wave-uniform
+      const int row = i * C::RPI + ld_row;
+      const int chunk = ld_pos ^ swz<C::CPR>(row);  // logical chunk landing at ld_pos
+      // rows past the end repeat the last row (finite); the softmax masks them
+      const int key = min(k0 + row, N - 1);
+      const long long off = (long long)key * p.k_sn + chunk * 8;
+      load_to_lds(kg + off, kl + i * 1024);
+      load_to_lds(vg + off, vl + i * 1024);
     }
   };
+  // loads this wave issues per tile (all waves that issue any issue this many)
+  constexpr int kLoadsPerTile = 2 * C::IPW;
 
   // ---- the three steps of a tile ----------------------------------------------
   // S^T = K Q^T for tile t
-  auto qk = [&](int t, f32x16_t (&s)[C::KB]) {
-    const unsigned char* k_lds = buf_of(t);
+  auto qk = [&](const unsigned char* __restrict__ k_lds, f32x16_t (&s)[C::KB]) {
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
@@ -302,7 +256,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
     for (int s_ = 0; s_ < C::KS; ++s_)
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
-        const u32x4_t a = *(const u32x4_t*)(k_lds + (kb * 32 + c) * C::K_STRIDE + s_ * 32 + h2 * 16);
+        const int row = kb * 32 + c;
+        const int chunk = (2 * s_ + h2) ^ swz<C::CPR>(row);
+        const u32x4_t a = *(const u32x4_t*)(k_lds + row * C::ROWB + chunk * 16);
         s[kb] = mfma_32x32x16(a, qreg[s_], s[kb]);
       }
   };
@@ -341,8 +297,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
     }
   };
   // P = 2^(s - m) rounded to bf16, l += rowsum(P), O^T += V^T P^T for tile t
-  auto pv = [&](int t, const f32x16_t (&s)[C::KB]) {
-    const unsigned char* vt_lds = buf_of(t) + C::K_BYTES;
+  auto pv = [&](const unsigned char* __restrict__ vt_lds, const f32x16_t (&s)[C::KB]) {  // V tile of tile j
     const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
     u32x4_t pop[C::PS];
     float rs0 = 0.f, rs1 = 0.f;
@@ -362,80 +317,119 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
       }
     }
     l_run += rs0 + rs1;
+    // V^T operand: lane l = 16 G + 4 t + u addresses V[key][d] with
+    // key = ps*16 + 8 r + 4 h2 + t and d = db*32 + 16 (G & 1) + 4 u; the
+    // transpose read then gives lane l the keys ps*16 + 8 r + 4 h2 + 0..3 of
+    // dimension db*32 + l % 32.
+    const int tr_t = (lane >> 2) & 3, tr_u = lane & 3, tr_g = (lane >> 4) & 1;
 #pragma unroll
     for (int ps = 0; ps < C::PS; ++ps)
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
-        const u32x4_t a = *(const u32x4_t*)(vt_lds + vt_off<C::GR, C::V_STRIDE>(db * 32 + c, ps * 16 + h2 * 8));
+        u32x4_t a;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int key = ps * 16 + 8 * r + 4 * h2 + tr_t;
+          const int d = db * 32 + 16 * tr_g + 4 * tr_u;
+          const int chunk = (d >> 3) ^ swz<C::CPR>(key);
+          const s16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4_t*)(vt_lds + key * C::ROWB + chunk * 16 + ((d >> 2) & 1) * 8));
+          const u32x2_t xx = __builtin_bit_cast(u32x2_t, x);
+          a[2 * r] = xx[0];
+          a[2 * r + 1] = xx[1];
+        }
         oacc[db] = mfma_32x32x16(a, pop[ps], oacc[db]);
       }
   };
 
-  // ---- prologue: tiles 0 and 1 staged, scores of tile 0 --------------------------
+  // ---- prologue: tiles 0, 1, 2 in flight; scores of tile 0 -------------------------
   f32x16_t sa[C::KB], sb[C::KB];
-  load_tile(0);
-  store_tile(0);
-  if (n_tiles > 1) {
-    load_tile(BN);
-    store_tile(1);
+  issue_tile(0, buf_of(0));
+  if (n_tiles > 1) issue_tile(1, buf_of(1));
+  if (n_tiles > 2) {
+    issue_tile(2, buf_of(2));
+    wait_vmcnt<kLoadsPerTile>();  // tiles 0 and 1 have landed
+  } else {
+    wait_vmcnt<0>();
   }
   __syncthreads();
   if (wave_tiles > 0) {
-    qk(0, sa);
+    qk(buf_of(0), sa);
     prep(0, sa);
   }
 
   // ---- main loop: iteration j consumes tile j and computes the scores of j+1 -------
   // Every wave runs n_tiles iterations (one barrier each); the loops only
-  // differ in how much of the tile work the wave still has.
-  auto staging = [&](int j) {
-    if (j + 2 < n_tiles) load_tile((j + 2) * BN);
+  // differ in how much of the tile work the wave still has. Tile j+3 is
+  // issued at the top of iteration j into the buffer tile j-1 used; tile j+2
+  // must have landed before the barrier that ends iteration j. The buffers
+  // reach the steps as distinct restrict pointers, which tells the compiler
+  // that reading tiles j and j+1 need not wait for the copy into j+3.
+  auto end_iteration = [&](int j) {
+    if (j + 3 < n_tiles)
+      wait_vmcnt<kLoadsPerTile>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();
   };
-  auto staging_store = [&](int j) {
-    if (j + 2 < n_tiles) store_tile(j + 2);
+  // b_issue: buffer receiving tile j+3; b_k: K tile of tile j+1; b_v: V tile of tile j
+  auto full_step = [&](int j, unsigned char* __restrict__ b_issue, const unsigned char* __restrict__ b_k,
+                       const unsigned char* __restrict__ b_v) {
+    if (j + 3 < n_tiles) issue_tile(j + 3, b_issue);
+    qk(b_k, sb);  // scores of tile j+1, in flight while tile j is exponentiated
+    pv(b_v, sa);
+  };
+  auto last_step = [&](int j, unsigned char* __restrict__ b_issue, const unsigned char* __restrict__ b_v) {
+    if (j + 3 < n_tiles) issue_tile(j + 3, b_issue);
+    pv(b_v, sa);
   };
   int j = 0;
   for (; j + 1 < wave_tiles; ++j) {  // tiles j and j+1 both have work for this wave
-    staging(j);
-    qk(j + 1, sb);  // in flight while tile j is exponentiated
-    pv(j, sa);
-    staging_store(j);
+    full_step(j, buf_of(j + 3), buf_of(j + 1), buf_of(j) + C::TILE);
     prep(j + 1, sb);
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) sa[kb] = sb[kb];
-    __syncthreads();
+    end_iteration(j);
   }
   if (j < wave_tiles) {  // the wave's last tile
-    staging(j);
-    pv(j, sa);
-    staging_store(j);
-    __syncthreads();
+    last_step(j, buf_of(j + 3), buf_of(j) + C::TILE);
+    end_iteration(j);
     ++j;
   }
-  for (; j < n_tiles; ++j) {  // no work left for this wave: keep staging tiles for the others
-    staging(j);
-    staging_store(j);
-    __syncthreads();
+  for (; j < n_tiles; ++j) {  // no work left for this wave: keep loading tiles for the others
+    if (j + 3 < n_tiles) issue_tile(j + 3, buf_of(j + 3));
+    end_iteration(j);
   }
 
-  // ---- epilogue: O / l -> bf16 ---------------------------------------------------
-  __bf16* __restrict__ og = (__bf16*)p.o + b * p.o_sb + h * p.o_sh;
+  // ---- epilogue: O / l -> bf16, written as whole rows through LDS ---------------------
+  // (every wave has passed the last barrier with no copy in flight, so the tile
+  // buffers are free)
+  constexpr int OROW = C::OROW;
+  unsigned char* const ost = lds + wave * 32 * OROW;
   const float l_tot = halves_sum(l_run);
-  if (qi < N) {
-    const float inv = 1.f / l_tot;
+  const float inv = 1.f / l_tot;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+  for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int vq = 0; vq < 4; ++vq) {
-        u32x2_t pk;
-        pk[0] = pack_bf16x2(oacc[db][vq * 4 + 0] * inv, oacc[db][vq * 4 + 1] * inv);
-        pk[1] = pack_bf16x2(oacc[db][vq * 4 + 2] * inv, oacc[db][vq * 4 + 3] * inv);
-        *(u32x2_t*)(og + (long long)qi * p.o_sn + db * 32 + vq * 8 + h2 * 4) = pk;
-      }
-    // m_ref is in units of scale * log2(e) * q.k (the sign fold leaves that product unchanged)
-    if (p.lse && h2 == 0)
-      p.lse[((long long)b * p.Hq + h) * N + qi] = (m_ref + __log2f(l_tot)) * 0.69314718055994531f;
+    for (int vq = 0; vq < 4; ++vq) {
+      u32x2_t pk;
+      pk[0] = pack_bf16x2(oacc[db][vq * 4 + 0] * inv, oacc[db][vq * 4 + 1] * inv);
+      pk[1] = pack_bf16x2(oacc[db][vq * 4 + 2] * inv, oacc[db][vq * 4 + 3] * inv);
+      *(u32x2_t*)(ost + c * OROW + (db * 32 + vq * 8 + h2 * 4) * 2) = pk;
+    }
+  __builtin_amdgcn_wave_barrier();
+  __bf16* __restrict__ og = (__bf16*)p.o + b * p.o_sb + h * p.o_sh;
+  constexpr int CPR = D / 8;        // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;     // rows per wave instruction
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / CPR, ch = lane % CPR;
+    const u32x4_t val = *(const u32x4_t*)(ost + r * OROW + ch * 16);
+    if (qw0 + r < N) *(u32x4_t*)(og + (long long)(qw0 + r) * p.o_sn + ch * 8) = val;
   }
+  // m_ref is in units of scale * log2(e) * q.k (the sign fold leaves that product unchanged)
+  if (p.lse && h2 == 0 && qi < N)
+    p.lse[((long long)b * p.Hq + h) * N + qi] = (m_ref + __log2f(l_tot)) * 0.69314718055994531f;
 }
 
 template <int D, int NW, int BN>
