@@ -374,22 +374,34 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   };
   // b_issue: buffer receiving tile j+3; b_k: K tile of tile j+1; b_v: V tile of tile j
   auto full_step = [&](int j, unsigned char* __restrict__ b_issue, const unsigned char* __restrict__ b_k,
-                       const unsigned char* __restrict__ b_v) {
+                       const unsigned char* __restrict__ b_v, const f32x16_t (&s_cur)[C::KB],
+                       f32x16_t (&s_nxt)[C::KB]) {
     if (j + 3 < n_tiles) issue_tile(j + 3, b_issue);
-    qk(b_k, sb);  // scores of tile j+1, in flight while tile j is exponentiated
-    pv(b_v, sa);
+    qk(b_k, s_nxt);  // scores of tile j+1, in flight while tile j is exponentiated
+    pv(b_v, s_cur);
   };
   auto last_step = [&](int j, unsigned char* __restrict__ b_issue, const unsigned char* __restrict__ b_v) {
     if (j + 3 < n_tiles) issue_tile(j + 3, b_issue);
     pv(b_v, sa);
   };
   int j = 0;
-  for (; j + 1 < wave_tiles; ++j) {  // tiles j and j+1 both have work for this wave
-    full_step(j, buf_of(j + 3), buf_of(j + 1), buf_of(j) + C::TILE);
+  // tiles j and j+1 both have work for this wave; unrolled by two so the
+  // score registers alternate instead of being copied
+  for (; j + 2 < wave_tiles; j += 2) {
+    full_step(j, buf_of(j + 3), buf_of(j + 1), buf_of(j) + C::TILE, sa, sb);
+    prep(j + 1, sb);
+    end_iteration(j);
+    full_step(j + 1, buf_of(j + 4), buf_of(j + 2), buf_of(j + 1) + C::TILE, sb, sa);
+    prep(j + 2, sa);
+    end_iteration(j + 1);
+  }
+  if (j + 1 < wave_tiles) {
+    full_step(j, buf_of(j + 3), buf_of(j + 1), buf_of(j) + C::TILE, sa, sb);
     prep(j + 1, sb);
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) sa[kb] = sb[kb];
     end_iteration(j);
+    ++j;
   }
   if (j < wave_tiles) {  // the wave's last tile
     last_step(j, buf_of(j + 3), buf_of(j) + C::TILE);
