@@ -110,10 +110,10 @@ struct Cfg {
   static constexpr int LPT = BN / RPI;     // load instructions per tensor per tile
   static constexpr int IPW = (LPT + NW - 1) / NW;  // of which one wave issues at most
   static constexpr int TILE = BN * ROWB;   // bytes of one K (or V) tile
-  static constexpr int STAGE = 2 * TILE;   // one LDS buffer: K tile then V tile
-  static constexpr int NBUF = 4;
+  static constexpr int NBUF = 4;           // ring of tile buffers
+  static constexpr int VREG = NBUF * TILE; // K tiles at [0, VREG), V tiles at [VREG, 2 VREG)
   static constexpr int OROW = D * 2 + 16;  // padded bytes per staged output row
-  static constexpr int LDS_BYTES = (NBUF * STAGE > NW * 32 * OROW) ? NBUF * STAGE : NW * 32 * OROW;
+  static constexpr int LDS_BYTES = (2 * VREG > NW * 32 * OROW) ? 2 * VREG : NW * 32 * OROW;
   static_assert(LPT % NW == 0 || NW % LPT == 0, "uneven tile loads");
   static_assert(BN % 32 == 0 && (D == 64 || D == 128), "bad tile");
 };
@@ -221,29 +221,83 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   const int wave_tiles = (qw0 >= N) ? 0 : (p.causal ? min(n_tiles, (qw0 + 31) / BN + 1) : n_tiles);
 
   // ---- HBM -> LDS copies of K/V tiles ----------------------------------------------
-  auto buf_of = [&](int t) { return lds + (t % C::NBUF) * C::STAGE; };
-  // this lane's part of a load instruction: tile-local row and logical chunk
+  // Buffer i of the ring: K tile at lds + i*TILE, V tile VREG bytes further.
+  // With the K and V tiles in separate halves every LDS read below is a
+  // per-lane register plus an immediate offset below 64 KiB, so once the ring
+  // position is a compile-time constant no address arithmetic is left.
+  auto kbuf = [&](int t) { return lds + (t % C::NBUF) * C::TILE; };
+  auto vbuf = [&](int t) { return lds + C::VREG + (t % C::NBUF) * C::TILE; };
+  // This lane's part of a load instruction: tile-local row, logical chunk and
+  // the byte offset from the tile's first row (rows are k_sn elements apart).
   const int ld_row = lane / C::CPR;
   const int ld_pos = lane % C::CPR;
+  const unsigned row_bytes = (unsigned)p.k_sn * 2u;
+  unsigned ld_off[C::IPW];
+#pragma unroll
+  for (int u = 0; u < C::IPW; ++u) {
+    const int row = (wave + u * NW) * C::RPI + ld_row;
+    ld_off[u] = (unsigned)row * row_bytes + (unsigned)(ld_pos ^ swz<C::CPR>(row)) * 16u;
+  }
   // issue the copies of tile t (this wave's share: instructions wave, wave+NW, ...)
   auto issue_tile = [&](int t, unsigned char* __restrict__ kl) {
     const int k0 = t * BN;
-    unsigned char* const vl = kl + C::TILE;
+    unsigned char* const vl = kl + C::VREG;
+    const char* const kt = (const char*)kg + (long long)k0 * row_bytes;  // wave-uniform
+    const char* const vt = (const char*)vg + (long long)k0 * row_bytes;
+    const bool ragged = k0 + BN > N;
 #pragma unroll
     for (int u = 0; u < C::IPW; ++u) {
       const int i = wave + u * NW;
       if (C::LPT < NW && i >= C::LPT) break;  // wave-uniform
-      const int row = i * C::RPI + ld_row;
-      const int chunk = ld_pos ^ swz<C::CPR>(row);  // logical chunk landing at ld_pos
-      // rows past the end repeat the last row (finite); the softmax masks them
-      const int key = min(k0 + row, N - 1);
-      const long long off = (long long)key * p.k_sn + chunk * 8;
-      load_to_lds(kg + off, kl + i * 1024);
-      load_to_lds(vg + off, vl + i * 1024);
+      unsigned off = ld_off[u];
+      if (ragged) {
+        // rows past the end repeat the last row (finite); the softmax masks them
+        const int row = i * C::RPI + ld_row;
+        const int chunk = ld_pos ^ swz<C::CPR>(row);
+        off = (unsigned)min(row, N - 1 - k0) * row_bytes + (unsigned)chunk * 16u;
+      }
+      load_to_lds(kt + off, kl + i * 1024);
+      load_to_lds(vt + off, vl + i * 1024);
     }
   };
   // loads this wave issues per tile (all waves that issue any issue this many)
   constexpr int kLoadsPerTile = 2 * C::IPW;
+
+  // ---- per-lane parts of the LDS read addresses (bytes from a tile's start) ------
+  // K operand of k-step s: row c (+32 per key block), chunk (2s + h2) ^ swz(c).
+  unsigned kpart[C::KS];
+#pragma unroll
+  for (int s_ = 0; s_ < C::KS; ++s_)
+    kpart[s_] = (unsigned)(c * C::ROWB + (((2 * s_ + h2) ^ swz<C::CPR>(c)) * 16));
+  // V^T operand: lane l = 16 G + 4 t + u addresses V[key][d] with
+  // key = ps*16 + 8 r + 4 h2 + t and d = db*32 + 16 (G & 1) + 4 u; the
+  // transpose read then gives lane l the keys ps*16 + 8 r + 4 h2 + 0..3 of
+  // dimension db*32 + l % 32. The ps term is a multiple of 16 rows, which the
+  // swizzle ignores, so it is an immediate offset. The parts include the V
+  // half's base VREG, leaving ring position and ps to the 16-bit immediate.
+  unsigned vpart[2][C::DB];
+  {
+    const int tr_t = (lane >> 2) & 3, tr_u = lane & 3, tr_g = (lane >> 4) & 1;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        const int key = 8 * r + 4 * h2 + tr_t;
+        const int d = db * 32 + 16 * tr_g + 4 * tr_u;
+        vpart[r][db] = (unsigned)(C::VREG + key * C::ROWB + ((d >> 3) ^ swz<C::CPR>(key)) * 16 + ((d >> 2) & 1) * 8);
+      }
+  }
+  // Hide the lane parts from loop-invariant code motion once per tile step:
+  // otherwise every (buffer, read) address of the unrolled loop is hoisted
+  // into a register of its own, far more than the register file holds.
+  auto refresh_parts = [&]() {
+#pragma unroll
+    for (int s_ = 0; s_ < C::KS; ++s_) asm volatile("" : "+v"(kpart[s_]));
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) asm volatile("" : "+v"(vpart[r][db]));
+  };
 
   // ---- the three steps of a tile ----------------------------------------------
   // S^T = K Q^T for tile t
@@ -252,15 +306,28 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+    // operands of k-step s+1 are read before the products of k-step s
+    u32x4_t a[2][C::KB];
 #pragma unroll
-    for (int s_ = 0; s_ < C::KS; ++s_)
+    for (int kb = 0; kb < C::KB; ++kb) a[0][kb] = *(const u32x4_t*)(k_lds + kpart[0] + kb * 32 * C::ROWB);
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        const int row = kb * 32 + c;
-        const int chunk = (2 * s_ + h2) ^ swz<C::CPR>(row);
-        const u32x4_t a = *(const u32x4_t*)(k_lds + row * C::ROWB + chunk * 16);
-        s[kb] = mfma_32x32x16(a, qreg[s_], s[kb]);
+    for (int s_ = 0; s_ < C::KS; ++s_) {
+      if (s_ + 1 < C::KS) {
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+          a[(s_ + 1) & 1][kb] = *(const u32x4_t*)(k_lds + kpart[s_ + 1] + kb * 32 * C::ROWB);
       }
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) s[kb] = mfma_32x32x16(a[s_ & 1][kb], qreg[s_], s[kb]);
+    }
+    // keep the reads one k-step ahead of the products (the scheduler would
+    // otherwise reuse one operand register and wait on every read)
+    __builtin_amdgcn_sched_group_barrier(0x100, C::KB, 0);
+#pragma unroll
+    for (int s_ = 0; s_ < C::KS; ++s_) {
+      if (s_ + 1 < C::KS) __builtin_amdgcn_sched_group_barrier(0x100, C::KB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, C::KB, 0);
+    }
   };
   // mask tile t where it reaches past the diagonal or the end, then move the
   // reference max if this tile's max exceeds it by more than the threshold
@@ -317,11 +384,6 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
       }
     }
     l_run += rs0 + rs1;
-    // V^T operand: lane l = 16 G + 4 t + u addresses V[key][d] with
-    // key = ps*16 + 8 r + 4 h2 + t and d = db*32 + 16 (G & 1) + 4 u; the
-    // transpose read then gives lane l the keys ps*16 + 8 r + 4 h2 + 0..3 of
-    // dimension db*32 + l % 32.
-    const int tr_t = (lane >> 2) & 3, tr_u = lane & 3, tr_g = (lane >> 4) & 1;
 #pragma unroll
     for (int ps = 0; ps < C::PS; ++ps)
 #pragma unroll
@@ -329,11 +391,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
         u32x4_t a;
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
-          const int key = ps * 16 + 8 * r + 4 * h2 + tr_t;
-          const int d = db * 32 + 16 * tr_g + 4 * tr_u;
-          const int chunk = (d >> 3) ^ swz<C::CPR>(key);
           const s16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4_t*)(vt_lds + key * C::ROWB + chunk * 16 + ((d >> 2) & 1) * 8));
+              (__attribute__((address_space(3))) s16x4_t*)(vt_lds - C::VREG + vpart[r][db] + ps * 16 * C::ROWB));
           const u32x2_t xx = __builtin_bit_cast(u32x2_t, x);
           a[2 * r] = xx[0];
           a[2 * r + 1] = xx[1];
@@ -344,17 +403,17 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
 
   // ---- prologue: tiles 0, 1, 2 in flight; scores of tile 0 -------------------------
   f32x16_t sa[C::KB], sb[C::KB];
-  issue_tile(0, buf_of(0));
-  if (n_tiles > 1) issue_tile(1, buf_of(1));
+  issue_tile(0, kbuf(0));
+  if (n_tiles > 1) issue_tile(1, kbuf(1));
   if (n_tiles > 2) {
-    issue_tile(2, buf_of(2));
+    issue_tile(2, kbuf(2));
     wait_vmcnt<kLoadsPerTile>();  // tiles 0 and 1 have landed
   } else {
     wait_vmcnt<0>();
   }
   __syncthreads();
   if (wave_tiles > 0) {
-    qk(buf_of(0), sa);
+    qk(kbuf(0), sa);
     prep(0, sa);
   }
 
@@ -376,6 +435,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   auto full_step = [&](int j, unsigned char* __restrict__ b_issue, const unsigned char* __restrict__ b_k,
                        const unsigned char* __restrict__ b_v, const f32x16_t (&s_cur)[C::KB],
                        f32x16_t (&s_nxt)[C::KB]) {
+    refresh_parts();
     if (j + 3 < n_tiles) issue_tile(j + 3, b_issue);
     qk(b_k, s_nxt);  // scores of tile j+1, in flight while tile j is exponentiated
     pv(b_v, s_cur);
@@ -384,32 +444,38 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
     if (j + 3 < n_tiles) issue_tile(j + 3, b_issue);
     pv(b_v, sa);
   };
+  // Tiles j .. j+4 all have work for this wave: unrolled by four, so the
+  // ring positions are compile-time constants (j is a multiple of four) and
+  // the score registers alternate instead of being copied.
   int j = 0;
-  // tiles j and j+1 both have work for this wave; unrolled by two so the
-  // score registers alternate instead of being copied
-  for (; j + 2 < wave_tiles; j += 2) {
-    full_step(j, buf_of(j + 3), buf_of(j + 1), buf_of(j) + C::TILE, sa, sb);
+  for (; j + 4 < wave_tiles; j += 4) {
+    full_step(j, kbuf(3), kbuf(1), vbuf(0), sa, sb);
     prep(j + 1, sb);
     end_iteration(j);
-    full_step(j + 1, buf_of(j + 4), buf_of(j + 2), buf_of(j + 1) + C::TILE, sb, sa);
+    full_step(j + 1, kbuf(0), kbuf(2), vbuf(1), sb, sa);
     prep(j + 2, sa);
     end_iteration(j + 1);
+    full_step(j + 2, kbuf(1), kbuf(3), vbuf(2), sa, sb);
+    prep(j + 3, sb);
+    end_iteration(j + 2);
+    full_step(j + 3, kbuf(2), kbuf(0), vbuf(3), sb, sa);
+    prep(j + 4, sa);
+    end_iteration(j + 3);
   }
-  if (j + 1 < wave_tiles) {
-    full_step(j, buf_of(j + 3), buf_of(j + 1), buf_of(j) + C::TILE, sa, sb);
+  for (; j + 1 < wave_tiles; ++j) {
+    full_step(j, kbuf(j + 3), kbuf(j + 1), vbuf(j), sa, sb);
     prep(j + 1, sb);
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) sa[kb] = sb[kb];
     end_iteration(j);
-    ++j;
   }
   if (j < wave_tiles) {  // the wave's last tile
-    last_step(j, buf_of(j + 3), buf_of(j) + C::TILE);
+    last_step(j, kbuf(j + 3), vbuf(j));
     end_iteration(j);
     ++j;
   }
   for (; j < n_tiles; ++j) {  // no work left for this wave: keep loading tiles for the others
-    if (j + 3 < n_tiles) issue_tile(j + 3, buf_of(j + 3));
+    if (j + 3 < n_tiles) issue_tile(j + 3, kbuf(j + 3));
     end_iteration(j);
   }
 
