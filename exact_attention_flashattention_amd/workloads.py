@@ -147,6 +147,102 @@ def paged_decode_inputs(B: int, Hq: int, Hkv: int, d: int, seq_lens, *, seed: in
                         name)
 
 
+@dataclasses.dataclass
+class ChunkInputs:
+    """A chunk of new tokens per sequence after a cached prefix (chunked
+    prefill). The pool holds the prefix; the chunk's own K/V are k_new/v_new,
+    which the append step writes into the pool before the attention runs."""
+    q: torch.Tensor            # [T, Hq, d], sequence b owns rows cu_q[b] .. cu_q[b+1]-1
+    k_new: torch.Tensor        # [T, Hkv, d]
+    v_new: torch.Tensor        # [T, Hkv, d]
+    k_pages: torch.Tensor      # [num_pages, page_size, Hkv, d]
+    v_pages: torch.Tensor
+    block_table: torch.Tensor  # int32 [B, max_pages_per_seq], pages for prefix + chunk
+    cu_q: torch.Tensor         # int32 [B + 1]
+    prefix_lens: torch.Tensor  # int32 [B], P_b
+    seq_lens: torch.Tensor     # int32 [B], P_b + c_b
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    page_size: int
+    max_pages_per_seq: int
+    max_q_len: int
+    scale: float
+    name: str = ""
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k_pages.shape[0])
+
+    @property
+    def total_q(self) -> int:
+        return int(self.q.shape[0])
+
+
+def chunked_prefill_inputs(B: int, Hq: int, Hkv: int, d: int, prefix_lens, chunk_lens, *,
+                           seed: int, page_size: int = PAGE_SIZE, permute: bool = True,
+                           max_pages_per_seq: Optional[int] = None,
+                           dtype: torch.dtype = torch.bfloat16,
+                           scale: Optional[float] = None, name: str = "") -> ChunkInputs:
+    """Draw a chunked-prefill problem. ``prefix_lens`` and ``chunk_lens`` are
+    lists of ints or inclusive ``(low, high)`` ranges drawn uniformly. The
+    lengths fix every shape, so they are drawn first (prefix, then chunk),
+    then q, k_new, v_new, the pool's K, the pool's V and the page permutation.
+    Sequence b owns ceil((P_b + c_b) / page_size) pages; its chunk slots in the
+    pool hold unrelated draws until the append overwrites them."""
+    g = _gen(seed)
+
+    def lengths(spec):
+        if isinstance(spec, tuple):
+            lo, hi = spec
+            return torch.randint(lo, hi + 1, (B,), generator=g, dtype=torch.int64).tolist()
+        out = [int(x) for x in spec]
+        assert len(out) == B
+        return out
+
+    P = lengths(prefix_lens)
+    c = lengths(chunk_lens)
+    T = sum(c)
+    q = _randn(g, (T, Hq, d), dtype)
+    k_new = _randn(g, (T, Hkv, d), dtype)
+    v_new = _randn(g, (T, Hkv, d), dtype)
+    L = [p + n for p, n in zip(P, c)]
+    pages_per = [-(-x // page_size) for x in L]
+    total = max(sum(pages_per), 1)
+    mpps = max(1, max(pages_per)) if max_pages_per_seq is None else max_pages_per_seq
+    assert mpps >= max(pages_per, default=0)
+    k_pages = _randn(g, (total, page_size, Hkv, d), dtype)
+    v_pages = _randn(g, (total, page_size, Hkv, d), dtype)
+    order = torch.randperm(total, generator=g).tolist() if permute else list(range(total))
+    table = torch.full((B, mpps), -1, dtype=torch.int32)
+    cursor = 0
+    for b in range(B):
+        n = pages_per[b]
+        if n:
+            table[b, :n] = torch.tensor(order[cursor:cursor + n], dtype=torch.int32)
+        cursor += n
+    cu = [0]
+    for n in c:
+        cu.append(cu[-1] + n)
+    return ChunkInputs(q, k_new, v_new, k_pages, v_pages, table,
+                       torch.tensor(cu, dtype=torch.int32), torch.tensor(P, dtype=torch.int32),
+                       torch.tensor(L, dtype=torch.int32), B, Hq, Hkv, d, page_size, mpps,
+                       max(c, default=0), 1.0 / math.sqrt(d) if scale is None else scale, name)
+
+
+def poison_chunk_slots(x: ChunkInputs, value: float = float("nan")) -> None:
+    """Fill every pool slot that is not part of a cached prefix with ``value``:
+    the chunk slots (until the append writes them), the slots past each
+    sequence's end, and pages no sequence references."""
+    keep = torch.zeros(x.k_pages.shape[0], x.page_size, dtype=torch.bool)
+    for b in range(x.B):
+        for t in range(int(x.prefix_lens[b])):
+            keep[int(x.block_table[b, t // x.page_size]), t % x.page_size] = True
+    x.k_pages[~keep] = value
+    x.v_pages[~keep] = value
+
+
 def poison_unused_slots(x: DecodeInputs, value: float = float("nan")) -> None:
     """Fill the slots past each sequence's end on its last page with ``value``
     (and any pool page no sequence references). A correct kernel never lets
@@ -165,8 +261,9 @@ def poison_unused_slots(x: DecodeInputs, value: float = float("nan")) -> None:
     x.v_pages[~used] = value
 
 
-# The five standard workloads. Index 1 is the small fp32 parity case; index 2
-# is the headline prefill; index 3 the MHA/MQA endpoints; 4 and 5 decode.
+# The standard workloads. Index 1 is the small fp32 parity case; index 2 is
+# the headline prefill; index 3 the MHA/MQA endpoints; 4 and 5 decode; 6 a
+# chunk of new tokens after a long cached prefix (paged prefill + append).
 
 def workload_1() -> PrefillInputs:
     return prefill_inputs(1, 128, 4, 2, 64, seed=43, dtype=torch.float32,
@@ -194,3 +291,9 @@ def workload_5() -> DecodeInputs:
     return paged_decode_inputs(4, 64, 8, 128, (98304, 131072), seed=47, permute=True,
                                max_pages_per_seq=131072 // PAGE_SIZE,
                                name="paged decode bf16 B=4 Hq=64 Hkv=8 d=128 seq_lens~U[98304,131072] page=16 permuted")
+
+
+def workload_6() -> ChunkInputs:
+    return chunked_prefill_inputs(4, 32, 8, 128, (6144, 14336), [2048] * 4, seed=48,
+                                  name="chunked prefill bf16 B=4 Hq=32 Hkv=8 d=128 prefix~U[6144,14336] "
+                                       "chunk=2048 page=16 permuted")
