@@ -13,6 +13,12 @@ is reported under "decode". Both are timed with HIP events recorded on the
 stream the kernels run on. The CPU baseline is the float64 oracle timed on a
 bounded sample of the same workloads on the host cores.
 
+Outside the timed step, "chunked_prefill" reports the chunked-prefill pair
+on its own workload (bf16, B=4, Hq=32, Hkv=8, d=128, a 2048-token chunk after
+a cached prefix of U[6144, 14336] tokens, permuted 16-token pages): the KV
+append in GB/s (new K/V rows read once and written once) and the paged
+prefill in TFLOP/s (visible (query, key) pairs, 4 d flops each).
+
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -45,6 +51,21 @@ def causal_flops(B, Hq, N, d) -> int:
 
 def kv_bytes(seq_lens, Hkv, d, elem=2) -> int:
     return int(sum(int(L) for L in seq_lens)) * Hkv * d * elem * 2
+
+
+def chunk_flops(x) -> int:
+    """Visible (query, key) pairs of a chunked prefill, 4 * d flops each:
+    row i of a chunk of c rows after P cached tokens sees P + i + 1 keys."""
+    pairs = 0
+    for P, L in zip(x.prefix_lens.tolist(), x.seq_lens.tolist()):
+        c = L - P
+        pairs += c * P + c * (c + 1) // 2
+    return 4 * x.Hq * x.d * pairs
+
+
+def append_bytes(x) -> int:
+    """K and V rows of the new tokens, read once and written once."""
+    return x.total_q * x.Hkv * x.d * 2 * 2 * 2
 
 
 def source_hash(*names) -> str:
@@ -98,6 +119,65 @@ def cpu_baseline(x2, x5, batches: int):
                   f"in {td:.2f} s",
         "decode_value": round(dg, 4), "decode_unit": "GB/s",
         "blas": "OpenBLAS (numpy)",
+    }
+
+
+def time_calls(fn, stream, warmup: int, steps: int) -> float:
+    """Average microseconds per call from HIP events on ``stream``."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / steps
+
+
+def chunked_setup(dev, stream):
+    """Resident inputs of the chunked-prefill workload and its two calls."""
+    import torch
+    import exact_attention_flashattention_amd as pkg
+    from exact_attention_flashattention_amd import workloads as wl
+    x = wl.workload_6()
+    q, kn, vn = x.q.to(dev), x.k_new.to(dev), x.v_new.to(dev)
+    kp, vp = x.k_pages.to(dev), x.v_pages.to(dev)
+    bt, cu, start, lens = (t.to(dev) for t in (x.block_table, x.cu_q, x.prefix_lens, x.seq_lens))
+    o = torch.empty_like(q)
+    append = lambda: pkg.attn_kv_append(kn, vn, kp, vp, bt, cu, start, max_new=x.max_q_len, stream=stream)
+    attend = lambda: pkg.attn_prefill_paged(q, kp, vp, bt, cu, lens, o, max_q_len=x.max_q_len,
+                                            scale=x.scale, stream=stream)
+    append()
+    torch.cuda.synchronize()
+    return x, append, attend
+
+
+def chunked_report(dev, stream, steps: int) -> dict:
+    """The chunked-prefill pair (KV append, then paged prefill), timed apart
+    from the step: it widens the path and is not part of `value`."""
+    x, append, attend = chunked_setup(dev, stream)
+    t_app = time_calls(append, stream, 3, steps)
+    t_att = time_calls(attend, stream, 3, steps)
+    fl = chunk_flops(x)
+    tf = fl / (t_att * 1e-6) / 1e12
+    by = append_bytes(x)
+    gb = by / (t_app * 1e-6) / 1e9
+    log(f"chunked: append {t_app:.1f} us ({gb:.0f} GB/s), paged prefill {t_att:.1f} us ({tf:.1f} TFLOP/s)")
+    return {
+        "workload": x.name, "seq_lens": x.seq_lens.tolist(), "prefix_lens": x.prefix_lens.tolist(),
+        "paged_prefill": {"value": round(tf, 3), "unit": "TFLOP/s", "avg_launch_us": round(t_att, 2),
+                          "flops_per_launch": fl,
+                          "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS,
+                                       "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                                       "kernel": "prefill_bf16_kernel<128,8,64,paged>"}},
+        "kv_append": {"value": round(gb, 2), "unit": "GB/s", "avg_launch_us": round(t_app, 2),
+                      "bytes_per_launch": by,
+                      "roofline": {"bound": "hbm", "achieved": round(gb, 2), "peak": HBM_PEAK_GBS,
+                                   "unit": "GB/s", "frac": round(gb / HBM_PEAK_GBS, 4),
+                                   "kernel": "kv_append_kernel"}},
     }
 
 
@@ -168,6 +248,11 @@ def only(args, dev) -> int:
         o = torch.empty_like(q)
         fn = lambda: pkg.attn_prefill(q, k, v, o, scale=x.scale, stream=stream)
         work = {"flops_per_launch": causal_flops(x.B, x.Hq, x.N, x.d)}
+    elif args.only in ("chunked", "append"):
+        x, append, attend = chunked_setup(dev, stream)
+        fn = attend if args.only == "chunked" else append
+        work = ({"flops_per_launch": chunk_flops(x)} if args.only == "chunked"
+                else {"bytes_per_launch": append_bytes(x)})
     elif args.only == "decode":
         x = wl.workload_5()
         t = [a.to(dev) for a in (x.q, x.k_pages, x.v_pages, x.block_table, x.seq_lens)]
@@ -192,7 +277,8 @@ def only(args, dev) -> int:
         fn()
     b.record(stream)
     torch.cuda.synchronize()
-    srcs = {"prefill": PREFILL_SOURCES, "decode": DECODE_SOURCES}.get(args.only)
+    srcs = {"prefill": PREFILL_SOURCES, "decode": DECODE_SOURCES, "chunked": PREFILL_SOURCES,
+            "append": ["kv_append.hip"]}.get(args.only)
     print(json.dumps({"only": args.only, "steps": args.steps,
                       "avg_us": round(a.elapsed_time(b) * 1e3 / args.steps, 2),
                       "source_sha256": source_hash(*srcs) if srcs else None, **work}), flush=True)
@@ -205,9 +291,11 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-chunked", action="store_true",
+                    help="skip the chunked-prefill (KV append + paged prefill) report")
     ap.add_argument("--cpu-batches", type=int, default=2,
                     help="batch entries of the headline prefill the CPU oracle is timed on")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "copy", "chunked", "append"], default=None,
                     help="launch only this kernel (for counter runs under rocprofv3); "
                          "'copy' is a plain 1 GiB device copy used to calibrate byte counters")
     ap.add_argument("--write-traffic", metavar="DIR", default=None,
@@ -322,8 +410,11 @@ def main() -> int:
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": dtraffic,
                          "kernel": "decode_split_kernel<128> + decode_merge_kernel<128>"},
         },
+        "chunked_prefill": None,
         "cpu_baseline": None,
     }
+    if not args.no_chunked:
+        result["chunked_prefill"] = chunked_report(dev, stream, max(10, args.steps // 2))
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(x2, x5, args.cpu_batches)

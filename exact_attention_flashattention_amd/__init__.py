@@ -1,4 +1,5 @@
-"""Exact causal GQA attention for MI355X (gfx950): prefill and paged decode.
+"""Exact causal GQA attention for MI355X (gfx950): prefill, paged decode,
+chunked prefill over a paged cache, and the KV append that feeds it.
 
 The computation lives in the HIP library libattn.so (C ABI in include/attn.h);
 this package only marshals torch GPU tensors into those calls. Nothing here
@@ -6,6 +7,6 @@ computes attention on the CPU.
 """
 from .binding import (  # noqa: F401
     AttnError, AttnLibraryMissing, LIB_PATH, attn_decode, attn_decode_num_splits,
-    attn_decode_workspace_size, attn_gather_pages, attn_prefill, attn_prefill_ex,
-    attn_status_string, lib,
+    attn_decode_workspace_size, attn_gather_pages, attn_kv_append, attn_prefill, attn_prefill_ex,
+    attn_prefill_paged, attn_status_string, lib,
 )

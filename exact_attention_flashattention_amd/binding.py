@@ -27,6 +27,9 @@ SIGNATURES = [
     ("attn_decode_num_splits", _i, [_i, _i, _i, _i]),
     ("attn_decode_workspace_size", _sz, [_i, _i, _i, _i, _i, _i]),
     ("attn_decode", _i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    ("attn_kv_append", _i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
+    ("attn_prefill_paged", _i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
+                                _i, _i, _f, _vp]),
     ("attn_gather_pages", _i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
     ("attn_status_string", ctypes.c_char_p, [_i]),
     ("attn_version", _i, []),
@@ -187,6 +190,78 @@ def attn_decode(q, k_pages, v_pages, block_table, seq_lens, o=None, *, scale: Op
                            float(d ** -0.5 if scale is None else scale), num_splits,
                            _dev(workspace, "workspace"), ws_bytes, _stream(stream))
     _check(st, "attn_decode")
+    return o
+
+
+def _check_pool(k_pages, v_pages, block_table, B):
+    import torch
+    if k_pages.dtype != torch.bfloat16 or v_pages.shape != k_pages.shape or v_pages.dtype != k_pages.dtype:
+        raise ValueError("k_pages and v_pages must be bf16 [num_pages, 16, Hkv, d] alike")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_pages]")
+
+
+def attn_kv_append(k_new, v_new, k_pages, v_pages, block_table, cu_new, start_pos, *,
+                   max_new: Optional[int] = None, stream=None):
+    """Write new tokens k_new/v_new [T, Hkv, d] (sequence b owns rows
+    cu_new[b] .. cu_new[b+1]-1, starting at cache position start_pos[b]) into
+    the bf16 page pools, in place. max_new defaults to the longest chunk
+    (read from cu_new on the host)."""
+    import torch
+    B = start_pos.shape[0]
+    _check_pool(k_pages, v_pages, block_table, B)
+    if cu_new.dtype != torch.int32 or start_pos.dtype != torch.int32 or cu_new.shape != (B + 1,):
+        raise ValueError("cu_new must be int32 [B + 1] and start_pos int32 [B]")
+    T, Hkv, d = k_new.shape
+    if v_new.shape != k_new.shape or k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
+        raise ValueError("k_new, v_new must be bf16 [T, Hkv, d] alike")
+    num_pages, page_size, Hkv2, d2 = k_pages.shape
+    if (Hkv2, d2) != (Hkv, d):
+        raise ValueError("pool and new rows disagree on Hkv or d")
+    if max_new is None:
+        max_new = int((cu_new[1:] - cu_new[:-1]).max().item()) if B else 0
+    st = lib().attn_kv_append(_dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_pages, "k_pages"),
+                              _dev(v_pages, "v_pages"), _dev(block_table, "block_table"),
+                              _dev(cu_new, "cu_new"), _dev(start_pos, "start_pos"), B, Hkv, d,
+                              page_size, block_table.shape[1], num_pages, T, max_new, _stream(stream))
+    _check(st, "attn_kv_append")
+
+
+def attn_prefill_paged(q, k_pages, v_pages, block_table, cu_q, seq_lens, o=None, *,
+                       max_q_len: Optional[int] = None, scale: Optional[float] = None, lse=None,
+                       stream=None):
+    """Chunk queries q [T, Hq, d] bf16 (sequence b owns rows cu_q[b] ..
+    cu_q[b+1]-1, at positions seq_lens[b] - c_b ..) against the paged cache.
+    Returns o [T, Hq, d]; lse, if given, is float32 [Hq, T]. max_q_len
+    defaults to the longest chunk (read from cu_q on the host)."""
+    import torch
+    B = seq_lens.shape[0]
+    _check_pool(k_pages, v_pages, block_table, B)
+    if cu_q.dtype != torch.int32 or seq_lens.dtype != torch.int32 or cu_q.shape != (B + 1,):
+        raise ValueError("cu_q must be int32 [B + 1] and seq_lens int32 [B]")
+    if q.dtype != torch.bfloat16 or q.dim() != 3:
+        raise ValueError("q must be bf16 [T, Hq, d]")
+    T, Hq, d = q.shape
+    num_pages, page_size, Hkv, d2 = k_pages.shape
+    if d2 != d:
+        raise ValueError("pool and q disagree on d")
+    if o is None:
+        o = torch.empty_like(q)
+    elif o.shape != q.shape or o.dtype != q.dtype:
+        raise ValueError("o must match q")
+    if max_q_len is None:
+        max_q_len = int((cu_q[1:] - cu_q[:-1]).max().item()) if B else 0
+    lse_ptr = None
+    if lse is not None:
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, T):
+            raise ValueError("lse must be float32 [Hq, T]")
+        lse_ptr = _dev(lse, "lse")
+    st = lib().attn_prefill_paged(_dev(q, "q"), _dev(k_pages, "k_pages"), _dev(v_pages, "v_pages"),
+                                  _dev(block_table, "block_table"), _dev(cu_q, "cu_q"),
+                                  _dev(seq_lens, "seq_lens"), _dev(o, "o"), lse_ptr, B, Hq, Hkv, d,
+                                  page_size, block_table.shape[1], num_pages, T, max_q_len,
+                                  float(d ** -0.5 if scale is None else scale), _stream(stream))
+    _check(st, "attn_prefill_paged")
     return o
 
 

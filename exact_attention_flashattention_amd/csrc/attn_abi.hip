@@ -54,11 +54,12 @@ int attn_prefill_ex(const void* q, const void* k, const void* v, void* o, float*
   if (layout != ATTN_BNHD && layout != ATTN_BHND) return ATTN_ERR_LAYOUT;
   if (!isfinite(scale)) return ATTN_ERR_SHAPE;
   if ((long long)B * N * Hq * d > kMaxElems) return ATTN_ERR_SHAPE;
+  if ((long long)Hkv * d >= (1 << 24)) return ATTN_ERR_SHAPE;  // key row offsets in a tile fit 32 bits
   if (dtype == ATTN_F32 && (Hq > 65535 || B > 65535)) return ATTN_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_ALIGN;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_ALIGN;
 
-  attn::PrefillParams p;
+  attn::PrefillParams p = {};
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
   p.B = B; p.N = N; p.Hq = Hq; p.Hkv = Hkv;
   const long long D = d;
@@ -134,6 +135,69 @@ int attn_decode(const void* q, const void* k_pages, const void* v_pages,
   p.num_splits = S;
   p.scale_log2 = scale * 1.4426950408889634f;
   const hipError_t e = attn::launch_decode(p, d, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                   const int32_t* block_table, const int32_t* cu_new, const int32_t* start_pos,
+                   int B, int Hkv, int d, int page_size, int max_pages_per_seq, int num_pages,
+                   int total_new, int max_new, void* stream) {
+  if (!k_new || !v_new || !k_pages || !v_pages || !block_table || !cu_new || !start_pos)
+    return ATTN_ERR_NULL;
+  if (B < 1 || B > 65535 || Hkv < 1 || max_pages_per_seq < 1 || num_pages < 1 || total_new < 0 ||
+      max_new < 0)
+    return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  if (page_size != 16) return ATTN_ERR_PAGE;
+  if ((long long)total_new * Hkv * d > kMaxElems || (long long)num_pages * page_size * Hkv * d > kMaxElems ||
+      (long long)max_pages_per_seq * page_size > 0x7fffffffLL)
+    return ATTN_ERR_SHAPE;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pages) || !aligned16(v_pages) ||
+      (reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(cu_new) & 3u) ||
+      (reinterpret_cast<uintptr_t>(start_pos) & 3u))
+    return ATTN_ERR_ALIGN;
+  if (total_new == 0 || max_new == 0) return ATTN_OK;  // nothing to write
+  const hipError_t e = attn::launch_kv_append(k_new, v_new, k_pages, v_pages, block_table, cu_new,
+                                              start_pos, B, Hkv, d, max_pages_per_seq, max_new,
+                                              reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_prefill_paged(const void* q, const void* k_pages, const void* v_pages,
+                       const int32_t* block_table, const int32_t* cu_q, const int32_t* seq_lens,
+                       void* o, float* lse, int B, int Hq, int Hkv, int d, int page_size,
+                       int max_pages_per_seq, int num_pages, int total_q, int max_q_len,
+                       float scale, void* stream) {
+  if (!q || !k_pages || !v_pages || !block_table || !cu_q || !seq_lens || !o) return ATTN_ERR_NULL;
+  if (B < 1 || max_pages_per_seq < 1 || num_pages < 1 || total_q < 0 || max_q_len < 0)
+    return ATTN_ERR_SHAPE;
+  int st = check_heads(Hq, Hkv);
+  if (st) return st;
+  if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  if (page_size != 16) return ATTN_ERR_PAGE;
+  if (!isfinite(scale)) return ATTN_ERR_SHAPE;
+  if ((long long)total_q * Hq * d > kMaxElems || (long long)num_pages * page_size * Hkv * d > kMaxElems ||
+      (long long)Hkv * d > (1 << 20) || (long long)max_pages_per_seq * page_size > 0x7fffffffLL ||
+      (long long)B * max_pages_per_seq > kMaxElems)
+    return ATTN_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o) ||
+      (reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(cu_q) & 3u) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return ATTN_ERR_ALIGN;
+  if (total_q == 0 || max_q_len == 0) return ATTN_OK;  // no query rows
+
+  attn::PrefillParams p = {};
+  p.q = q; p.k = k_pages; p.v = v_pages; p.o = o; p.lse = lse;
+  p.B = B; p.N = max_q_len; p.Hq = Hq; p.Hkv = Hkv;
+  p.q_sn = (long long)Hq * d; p.q_sh = d;
+  p.o_sn = p.q_sn; p.o_sh = p.q_sh;
+  p.k_sn = (long long)Hkv * d; p.k_sh = d;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.causal = 1;
+  p.cu_q = cu_q; p.seq_lens = seq_lens; p.block_table = block_table;
+  p.max_pages_per_seq = max_pages_per_seq;
+  p.total_q = total_q;
+  const hipError_t e = attn::launch_prefill_paged(p, d, max_q_len, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

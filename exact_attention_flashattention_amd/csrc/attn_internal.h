@@ -20,6 +20,15 @@ struct PrefillParams {
   long long o_sb, o_sn, o_sh;
   float scale_log2;  // scale * log2(e): scores are carried in base-2 units
   int causal;
+  // Paged variant only: q/o rows of sequence b are cu_q[b] .. cu_q[b+1]-1
+  // (strides q_sn/q_sh, o_sn/o_sh; q_sb, o_sb, k_sb unused), k/v are page
+  // pools [pages, 16, Hkv, d] with row stride k_sn = Hkv*d and head stride
+  // k_sh = d, and sequence b holds seq_lens[b] keys.
+  const int32_t* cu_q;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  int max_pages_per_seq;
+  int total_q;  // lse layout [Hq, total_q]
 };
 
 // One decode problem (bf16 pages, page_size 16).
@@ -37,6 +46,11 @@ struct DecodeParams {
 };
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream);
+hipError_t launch_prefill_paged(const PrefillParams& p, int d, int max_q_len, hipStream_t stream);
+hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                            const int32_t* block_table, const int32_t* cu_new,
+                            const int32_t* start_pos, int B, int Hkv, int d,
+                            int max_pages_per_seq, int max_new, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillParams& p, int d, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t stream);
 hipError_t launch_gather(const void* pages, const int32_t* block_table,

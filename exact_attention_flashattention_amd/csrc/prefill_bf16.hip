@@ -62,6 +62,7 @@ typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kPage = 16;  // tokens per page of a paged KV cache
 // Lazy-rescale threshold in base-2 exponent units: the running reference is
 // moved only when a row max exceeds it by more than this.
 constexpr float kRescaleTau = 8.0f;
@@ -144,7 +145,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((NCNT & 15) | ((NCNT >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int D, int NW, int BN>
+// PAGED = false: one [B, N, H, d] or [B, H, N, d] sequence per batch entry,
+// query row i at position i. PAGED = true: a chunk of queries per sequence
+// (rows cu_q[b] ..) at positions P_b + i, keys read through the block table.
+template <int D, int NW, int BN, bool PAGED>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams p, int n_qtiles) {
   using C = Cfg<D, NW, BN>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS_BYTES];
@@ -162,12 +166,15 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
     w = xcd * q8 + min(xcd, r8) + slot;
   }
   const int per_pair = n_qtiles * g;
-  const int pair = w / per_pair;            // (b, kv head)
+  // (kv head, b) pairs with b fastest: an XCD's contiguous range then holds
+  // the same KV heads of different sequences, which keeps the XCDs balanced
+  // when the sequences differ in length
+  const int pair = w / per_pair;
   const int rem = w - pair * per_pair;
   const int qtile = n_qtiles - 1 - rem / g; // heaviest causal tiles first
   const int hg = rem - (rem / g) * g;
-  const int b = pair / p.Hkv;
-  const int kvh = pair - b * p.Hkv;
+  const int kvh = pair / p.B;
+  const int b = pair - kvh * p.B;
   const int h = kvh * g + hg;
 
   const int tid = threadIdx.x;
@@ -176,8 +183,29 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   const int c = lane & 31;   // query column of S^T / O^T held by this lane
   const int h2 = lane >> 5;  // lane half
 
-  const int N = p.N;
   const int q_tile0 = qtile * C::BM;
+  // Nq query rows and Nk keys for this (b, h); P is the position of query
+  // row 0, so row i sees keys 0 .. P + i (causality compares positions).
+  int Nq, Nk, P;
+  const __bf16* qg;
+  __bf16* og;
+  long long lse_row0;
+  if constexpr (PAGED) {
+    const int r0 = p.cu_q[b];
+    Nq = p.cu_q[b + 1] - r0;
+    Nk = p.seq_lens[b];
+    P = max(Nk - Nq, 0);
+    qg = (const __bf16*)p.q + (long long)r0 * p.q_sn + h * p.q_sh;
+    og = (__bf16*)p.o + (long long)r0 * p.o_sn + h * p.o_sh;
+    lse_row0 = (long long)h * p.total_q + r0;
+  } else {
+    Nq = Nk = p.N;
+    P = 0;
+    qg = (const __bf16*)p.q + b * p.q_sb + h * p.q_sh;
+    og = (__bf16*)p.o + b * p.o_sb + h * p.o_sh;
+    lse_row0 = ((long long)b * p.Hq + h) * p.N;
+  }
+  if (q_tile0 >= Nq) return;  // the whole work-group: a chunk shorter than the launch
   // Query block of this wave. Waves w and w + 4 share a SIMD; pairing block w
   // with block NW - 1 - (w - 4) gives every SIMD one early and one late block,
   // so the causal work per SIMD is balanced.
@@ -185,9 +213,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   const int qw0 = q_tile0 + qblk * 32;  // first query row of this wave
   const int qi = qw0 + c;               // this lane's query row
 
-  const __bf16* __restrict__ qg = (const __bf16*)p.q + b * p.q_sb + h * p.q_sh;
-  const __bf16* __restrict__ kg = (const __bf16*)p.k + b * p.k_sb + kvh * p.k_sh;
-  const __bf16* __restrict__ vg = (const __bf16*)p.v + b * p.k_sb + kvh * p.k_sh;
+  // contiguous: this (b, kv head)'s row 0; paged: the pools' kv head offset
+  const __bf16* __restrict__ kg = (const __bf16*)p.k + (PAGED ? 0 : b * p.k_sb) + kvh * p.k_sh;
+  const __bf16* __restrict__ vg = (const __bf16*)p.v + (PAGED ? 0 : b * p.k_sb) + kvh * p.k_sh;
 
   // Scores are carried as raw q.k; c2 = scale * log2(e) > 0 is applied inside
   // the exponent. A negative scale is folded into Q by flipping its sign bits
@@ -201,7 +229,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   // ---- Q^T operand in registers ---------------------------------------------
   u32x4_t qreg[C::KS];
   {
-    const int qc = min(qi, N - 1);
+    const int qc = min(qi, Nq - 1);
 #pragma unroll
     for (int s = 0; s < C::KS; ++s)
       qreg[s] = *(const u32x4_t*)(qg + (long long)qc * p.q_sn + s * 16 + h2 * 8) ^ qflip;
@@ -215,10 +243,11 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
   float m_ref = kNegInf, l_run = 0.f;
 
-  const int q_last_wg = min(q_tile0 + C::BM, N) - 1;
-  const int n_tiles = p.causal ? (q_last_wg / BN + 1) : ((N + BN - 1) / BN);
+  const int q_last_wg = min(q_tile0 + C::BM, Nq) - 1;
+  const int k_tiles = (Nk + BN - 1) / BN;
+  const int n_tiles = p.causal ? min(k_tiles, (P + q_last_wg) / BN + 1) : k_tiles;
   // tiles 0 .. wave_tiles-1 hold keys visible to some row of this wave
-  const int wave_tiles = (qw0 >= N) ? 0 : (p.causal ? min(n_tiles, (qw0 + 31) / BN + 1) : n_tiles);
+  const int wave_tiles = (qw0 >= Nq) ? 0 : (p.causal ? min(n_tiles, (P + qw0 + 31) / BN + 1) : n_tiles);
 
   // ---- HBM -> LDS copies of K/V tiles ----------------------------------------------
   // Buffer i of the ring: K tile at lds + i*TILE, V tile VREG bytes further.
@@ -232,29 +261,48 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   const int ld_row = lane / C::CPR;
   const int ld_pos = lane % C::CPR;
   const unsigned row_bytes = (unsigned)p.k_sn * 2u;
+  // Paged: a load instruction covers RPI rows inside one 16-token page, so its
+  // page is wave-uniform and the lane offset is from the page's first token.
   unsigned ld_off[C::IPW];
 #pragma unroll
   for (int u = 0; u < C::IPW; ++u) {
     const int row = (wave + u * NW) * C::RPI + ld_row;
-    ld_off[u] = (unsigned)row * row_bytes + (unsigned)(ld_pos ^ swz<C::CPR>(row)) * 16u;
+    const int prow = PAGED ? (row & (kPage - 1)) : row;
+    ld_off[u] = (unsigned)prow * row_bytes + (unsigned)(ld_pos ^ swz<C::CPR>(row)) * 16u;
   }
+  // block table row of this sequence, read with scalar loads
+  const __attribute__((address_space(4))) int32_t* const table =
+      PAGED ? (const __attribute__((address_space(4))) int32_t*)(p.block_table + (long long)b * p.max_pages_per_seq)
+            : nullptr;
+  const long long page_bytes = (long long)row_bytes * kPage;
   // issue the copies of tile t (this wave's share: instructions wave, wave+NW, ...)
   auto issue_tile = [&](int t, unsigned char* __restrict__ kl) {
     const int k0 = t * BN;
     unsigned char* const vl = kl + C::VREG;
-    const char* const kt = (const char*)kg + (long long)k0 * row_bytes;  // wave-uniform
-    const char* const vt = (const char*)vg + (long long)k0 * row_bytes;
-    const bool ragged = k0 + BN > N;
+    const bool ragged = k0 + BN > Nk;
 #pragma unroll
     for (int u = 0; u < C::IPW; ++u) {
       const int i = wave + u * NW;
       if (C::LPT < NW && i >= C::LPT) break;  // wave-uniform
+      const char* kt;
+      const char* vt;
+      if constexpr (PAGED) {
+        // the page of this instruction's rows (the last key's page once past the end)
+        const int page = table[min(k0 + i * C::RPI, Nk - 1) / kPage];
+        kt = (const char*)kg + page * page_bytes;
+        vt = (const char*)vg + page * page_bytes;
+      } else {
+        kt = (const char*)kg + (long long)k0 * row_bytes;  // wave-uniform
+        vt = (const char*)vg + (long long)k0 * row_bytes;
+      }
       unsigned off = ld_off[u];
       if (ragged) {
-        // rows past the end repeat the last row (finite); the softmax masks them
+        // rows past the end repeat the last key's row (finite); the softmax masks them
         const int row = i * C::RPI + ld_row;
         const int chunk = ld_pos ^ swz<C::CPR>(row);
-        off = (unsigned)min(row, N - 1 - k0) * row_bytes + (unsigned)chunk * 16u;
+        const int key = min(k0 + row, Nk - 1);
+        const int prow = PAGED ? (key & (kPage - 1)) : key - k0;
+        off = (unsigned)prow * row_bytes + (unsigned)chunk * 16u;
       }
       load_to_lds(kt + off, kl + i * 1024);
       load_to_lds(vt + off, vl + i * 1024);
@@ -333,10 +381,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   // reference max if this tile's max exceeds it by more than the threshold
   auto prep = [&](int t, f32x16_t (&s)[C::KB]) {
     const int k0 = t * BN;
-    if ((p.causal && k0 + BN - 1 > qw0) || (k0 + BN > N)) {
+    if ((p.causal && k0 + BN - 1 > P + qw0) || (k0 + BN > Nk)) {
       // key k0 + h2*4 + off (off a compile-time constant per element) is visible
       // iff off <= lim
-      const int lim = (p.causal ? min(qi, N - 1) : N - 1) - k0 - h2 * 4;
+      const int lim = (p.causal ? min(P + qi, Nk - 1) : Nk - 1) - k0 - h2 * 4;
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
@@ -485,7 +533,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   constexpr int OROW = C::OROW;
   unsigned char* const ost = lds + wave * 32 * OROW;
   const float l_tot = halves_sum(l_run);
-  const float inv = 1.f / l_tot;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;  // a row with no key gets zeros
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -496,27 +544,27 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
       *(u32x2_t*)(ost + c * OROW + (db * 32 + vq * 8 + h2 * 4) * 2) = pk;
     }
   __builtin_amdgcn_wave_barrier();
-  __bf16* __restrict__ og = (__bf16*)p.o + b * p.o_sb + h * p.o_sh;
   constexpr int CPR = D / 8;        // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;     // rows per wave instruction
 #pragma unroll
   for (int i = 0; i < 32 / RPI; ++i) {
     const int r = i * RPI + lane / CPR, ch = lane % CPR;
     const u32x4_t val = *(const u32x4_t*)(ost + r * OROW + ch * 16);
-    if (qw0 + r < N) *(u32x4_t*)(og + (long long)(qw0 + r) * p.o_sn + ch * 8) = val;
+    if (qw0 + r < Nq) *(u32x4_t*)(og + (long long)(qw0 + r) * p.o_sn + ch * 8) = val;
   }
   // m_ref is in units of scale * log2(e) * q.k (the sign fold leaves that product unchanged)
-  if (p.lse && h2 == 0 && qi < N)
-    p.lse[((long long)b * p.Hq + h) * N + qi] = (m_ref + __log2f(l_tot)) * 0.69314718055994531f;
+  if (p.lse && h2 == 0 && qi < Nq)
+    p.lse[lse_row0 + qi] = (m_ref + __log2f(l_tot)) * 0.69314718055994531f;
 }
 
-template <int D, int NW, int BN>
-hipError_t launch_cfg(const PrefillParams& p, hipStream_t stream) {
+// n_rows: query rows per sequence (the longest chunk when paged)
+template <int D, int NW, int BN, bool PAGED>
+hipError_t launch_cfg(const PrefillParams& p, int n_rows, hipStream_t stream) {
   using C = Cfg<D, NW, BN>;
-  const int n_qtiles = (p.N + C::BM - 1) / C::BM;
+  const int n_qtiles = (n_rows + C::BM - 1) / C::BM;
   const long long total = (long long)p.B * p.Hq * n_qtiles;
   if (total <= 0 || total > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, BN>), dim3((unsigned)total), dim3(C::NT), 0,
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, BN, PAGED>), dim3((unsigned)total), dim3(C::NT), 0,
                      stream, p, n_qtiles);
   return hipGetLastError();
 }
@@ -532,8 +580,14 @@ hipError_t launch_cfg(const PrefillParams& p, hipStream_t stream) {
 #endif
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream) {
-  if (d == 128) return launch_cfg<128, ATTN_PREFILL_D128>(p, stream);
-  if (d == 64) return launch_cfg<64, ATTN_PREFILL_D64>(p, stream);
+  if (d == 128) return launch_cfg<128, ATTN_PREFILL_D128, false>(p, p.N, stream);
+  if (d == 64) return launch_cfg<64, ATTN_PREFILL_D64, false>(p, p.N, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_paged(const PrefillParams& p, int d, int max_q_len, hipStream_t stream) {
+  if (d == 128) return launch_cfg<128, ATTN_PREFILL_D128, true>(p, max_q_len, stream);
+  if (d == 64) return launch_cfg<64, ATTN_PREFILL_D64, true>(p, max_q_len, stream);
   return hipErrorInvalidValue;
 }
 

@@ -9,6 +9,10 @@
  *   attn_decode : one new query token per sequence against a KV cache stored in
  *       fixed-size pages addressed through a block table, split along the
  *       context and merged by log-sum-exp.
+ *   attn_prefill_paged : a chunk of new queries per sequence against the same
+ *       paged cache, each row seeing every key up to its own position (the
+ *       attention half of chunked prefill); attn_kv_append writes the chunk's
+ *       keys and values into the pages first.
  *
  * Definitions follow these pages (cited by title and section):
  *   [SDPA]  "Module 5. Modern Attention Mechanisms" (vladkulikov.com), section 4
@@ -170,6 +174,74 @@ int attn_decode(const void* q, const void* k_pages, const void* v_pages,
                 int B, int Hq, int Hkv, int d, int page_size, int max_pages_per_seq,
                 int num_pages, float scale, int num_splits,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_kv_append - write the keys and values of new tokens into the paged
+ * cache, the append step of [PAGED] (token t of sequence b goes to page
+ * block_table[b, t / page_size], slot t % page_size) [KV].
+ *
+ * k_new, v_new: [T, Hkv, d] bf16, the new tokens of all sequences packed row
+ *               after row; sequence b owns rows cu_new[b] .. cu_new[b+1]-1.
+ * k_pages,
+ * v_pages:      [num_pages, page_size, Hkv, d] bf16 (in/out); only the slots
+ *               of the new tokens are written, every other byte is left as is.
+ * block_table:  int32 [B, max_pages_per_seq] (device), as for attn_decode.
+ * cu_new:       int32 [B + 1] (device), non-decreasing, cu_new[0] = 0,
+ *               cu_new[B] = T.
+ * start_pos:    int32 [B] (device), position of sequence b's first new token
+ *               (the number of tokens cached before the append).
+ * total_new:    T, the rows of k_new and v_new (host).
+ * max_new:      an upper bound on cu_new[b+1] - cu_new[b] (host); rows beyond
+ *               it are not written.
+ * Preconditions checked on the device side only by the caller:
+ *   start_pos[b] + (cu_new[b+1] - cu_new[b]) <= max_pages_per_seq * page_size,
+ *   and every table entry that is written through lies in [0, num_pages).
+ * Requires page_size == 16 and d in {64, 128}. Pure data movement: the pool
+ * afterwards holds the new rows bit for bit.
+ */
+int attn_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                   const int32_t* block_table, const int32_t* cu_new, const int32_t* start_pos,
+                   int B, int Hkv, int d, int page_size, int max_pages_per_seq, int num_pages,
+                   int total_new, int max_new, void* stream);
+
+/*
+ * attn_prefill_paged - a chunk of new queries per sequence against a paged
+ * KV cache that already holds the sequence's earlier tokens and the chunk's
+ * own K/V (write those first with attn_kv_append): the attention half of a
+ * chunked prefill ("Module 09: Efficient Attention", section "Chunked
+ * Prefill: Bounding the Stall"). bf16 in, fp32 accumulation, bf16 out.
+ *
+ * q:           [T, Hq, d] bf16, the chunks of all sequences packed row after
+ *              row; sequence b owns rows cu_q[b] .. cu_q[b+1]-1 (c_b rows).
+ * k_pages,
+ * v_pages:     [num_pages, page_size, Hkv, d] bf16, as for attn_decode.
+ * block_table: int32 [B, max_pages_per_seq] (device).
+ * cu_q:        int32 [B + 1] (device), non-decreasing, cu_q[0] = 0, cu_q[B] = T.
+ * seq_lens:    int32 [B] (device), L_b: tokens cached for sequence b
+ *              including its chunk, so the chunk sits at positions
+ *              P_b = L_b - c_b .. L_b - 1.
+ * o:           [T, Hq, d] bf16 (out).
+ * lse:         NULL, or fp32 [Hq, T] (out), natural-log softmax denominator
+ *              of each row, as for attn_prefill_ex.
+ * total_q:     T, the rows of q and o (host); it fixes the lse layout.
+ * max_q_len:   an upper bound on every c_b (host); it sizes the launch.
+ * Row i of sequence b, query head h, sees the keys at positions 0 .. P_b + i
+ * (causality compares token positions [SDPA] section 4; after a prefix of P
+ * tokens row i is at position P + i):
+ *   o[cu_q[b]+i, h, :] = sum_{t <= P_b+i} softmax_t(scale * q.k_t) v_t,
+ * with k_t, v_t read through the block table [PAGED] and kv = floor(h / g).
+ * With P_b = 0 this is the causal prefill of the chunk alone.
+ * Preconditions checked on the device side only by the caller:
+ *   c_b <= L_b <= max_pages_per_seq * page_size, c_b <= max_q_len, and every
+ *   table entry that is read lies in [0, num_pages). A sequence with
+ *   c_b > L_b (violating the first) gets zeros for the rows that see no key.
+ * Requires page_size == 16, d in {64, 128}, Hq a multiple of Hkv.
+ */
+int attn_prefill_paged(const void* q, const void* k_pages, const void* v_pages,
+                       const int32_t* block_table, const int32_t* cu_q, const int32_t* seq_lens,
+                       void* o, float* lse, int B, int Hq, int Hkv, int d, int page_size,
+                       int max_pages_per_seq, int num_pages, int total_q, int max_q_len,
+                       float scale, void* stream);
 
 /*
  * attn_gather_pages - materialise the logical cache of each sequence from the

@@ -32,7 +32,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) == 8
+    assert len(names) == 10
     for n in names:
         assert hasattr(L, n), n
     assert sorted(n for n, _, _ in binding.SIGNATURES) == names
@@ -124,6 +124,56 @@ def test_gather_rejects(L):
     assert g(A, A, A, A, 1, 2, 64, 16, 4, 8, 10, 3, None) == ERR["ATTN_ERR_DTYPE"]
     assert g(A, A, A, A, 0, 2, 64, 16, 4, 8, 10, 2, None) == ERR["ATTN_ERR_SHAPE"]
     assert g(A + 4, A, A, A, 1, 2, 64, 16, 4, 8, 10, 2, None) == ERR["ATTN_ERR_ALIGN"]
+
+
+def append(L, **kw):
+    a = dict(kn=A, vn=A, kp=A, vp=A, table=A, cu=A, start=A, B=2, Hkv=2, d=64, page_size=16, mpps=4,
+             num_pages=8, total=10, max_new=5)
+    a.update(kw)
+    return L.attn_kv_append(a["kn"], a["vn"], a["kp"], a["vp"], a["table"], a["cu"], a["start"], a["B"],
+                            a["Hkv"], a["d"], a["page_size"], a["mpps"], a["num_pages"], a["total"],
+                            a["max_new"], None)
+
+
+@pytest.mark.parametrize("kw,err", [
+    (dict(kn=None), "ATTN_ERR_NULL"), (dict(cu=None), "ATTN_ERR_NULL"), (dict(start=None), "ATTN_ERR_NULL"),
+    (dict(B=0), "ATTN_ERR_SHAPE"), (dict(B=70000), "ATTN_ERR_SHAPE"), (dict(total=-1), "ATTN_ERR_SHAPE"),
+    (dict(max_new=-1), "ATTN_ERR_SHAPE"), (dict(d=96), "ATTN_ERR_HEAD_DIM"), (dict(page_size=32), "ATTN_ERR_PAGE"),
+    (dict(kp=A + 8), "ATTN_ERR_ALIGN"), (dict(cu=A + 2), "ATTN_ERR_ALIGN"),
+])
+def test_kv_append_rejects(L, kw, err):
+    assert append(L, **kw) == ERR[err]
+
+
+def test_kv_append_with_nothing_to_write_is_a_no_op(L):
+    # returns before any launch, so host pointers are fine here
+    assert append(L, total=0) == 0
+    assert append(L, max_new=0) == 0
+
+
+def paged(L, **kw):
+    a = dict(q=A, kp=A, vp=A, table=A, cu=A, lens=A, o=A, lse=None, B=2, Hq=8, Hkv=2, d=128,
+             page_size=16, mpps=4, num_pages=8, total=10, max_q=5, scale=0.1)
+    a.update(kw)
+    return L.attn_prefill_paged(a["q"], a["kp"], a["vp"], a["table"], a["cu"], a["lens"], a["o"], a["lse"],
+                                a["B"], a["Hq"], a["Hkv"], a["d"], a["page_size"], a["mpps"],
+                                a["num_pages"], a["total"], a["max_q"], a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,err", [
+    (dict(q=None), "ATTN_ERR_NULL"), (dict(cu=None), "ATTN_ERR_NULL"), (dict(lens=None), "ATTN_ERR_NULL"),
+    (dict(B=0), "ATTN_ERR_SHAPE"), (dict(mpps=0), "ATTN_ERR_SHAPE"), (dict(total=-2), "ATTN_ERR_SHAPE"),
+    (dict(Hq=6, Hkv=4), "ATTN_ERR_GQA"), (dict(d=32), "ATTN_ERR_HEAD_DIM"), (dict(page_size=8), "ATTN_ERR_PAGE"),
+    (dict(scale=float("inf")), "ATTN_ERR_SHAPE"), (dict(o=A + 4), "ATTN_ERR_ALIGN"),
+    (dict(lse=A + 2), "ATTN_ERR_ALIGN"), (dict(lens=A + 1), "ATTN_ERR_ALIGN"),
+])
+def test_prefill_paged_rejects(L, kw, err):
+    assert paged(L, **kw) == ERR[err]
+
+
+def test_prefill_paged_with_no_rows_is_a_no_op(L):
+    assert paged(L, total=0) == 0
+    assert paged(L, max_q=0) == 0
 
 
 def test_binding_refuses_cpu_tensors():

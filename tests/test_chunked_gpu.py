@@ -1,0 +1,164 @@
+"""Chunked prefill on the GPU: the KV append and the paged prefill (through
+the C ABI) against the CPU float64 oracle.
+
+The append is data movement and must be bit-exact, including every slot it
+must not touch. The paged prefill is compared element by element on ragged
+shapes (chunks shorter than a tile, spanning several query tiles, prefixes
+off page and tile boundaries, an empty chunk) with every pool slot outside a
+cached prefix poisoned with NaN before the append, on sampled rows at the
+full chunked-prefill workload, and bit for bit against the contiguous
+prefill when there is no prefix.
+
+Tolerances against the fp64 oracle: bf16 inputs, fp32 accumulation,
+max-abs <= 2e-2 and mean-abs <= 5e-3; lse max-abs <= 1e-2.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_flashattention_amd import binding as bd
+from exact_attention_flashattention_amd import workloads as wl
+from oracle import attention_oracle as ao
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX, BF16_MEAN = 2e-2, 5e-3
+LSE_BF16 = 1e-2
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def gpu_append(x: wl.ChunkInputs):
+    kp, vp = x.k_pages.cuda(), x.v_pages.cuda()
+    bt, cu, start = x.block_table.cuda(), x.cu_q.cuda(), x.prefix_lens.cuda()
+    bd.attn_kv_append(x.k_new.cuda(), x.v_new.cuda(), kp, vp, bt, cu, start)
+    return kp, vp, bt, cu
+
+
+def gpu_chunk(x: wl.ChunkInputs, lse=True):
+    kp, vp, bt, cu = gpu_append(x)
+    l = torch.full((x.Hq, x.total_q), float("nan"), device="cuda") if lse else None
+    o = bd.attn_prefill_paged(x.q.cuda(), kp, vp, bt, cu, x.seq_lens.cuda(), scale=x.scale, lse=l)
+    torch.cuda.synchronize()
+    return o.cpu(), (l.cpu() if lse else None), kp.cpu(), vp.cpu()
+
+
+CASES = [
+    # B, Hq, Hkv, d, prefix lengths, chunk lengths
+    (1, 4, 2, 128, [0], [1]),                          # one token, no prefix
+    (2, 4, 4, 64, [5, 17], [7, 3]),                    # short chunks off page boundaries
+    (3, 8, 2, 128, [0, 64, 100], [64, 1, 300]),        # tile-aligned prefix; 2 query tiles
+    (2, 8, 1, 64, [33, 1000], [129, 77]),              # MQA, 32-key tiles
+    (4, 8, 8, 128, [15, 16, 17, 250], [1, 16, 31, 65]),  # MHA, around a page boundary
+    (3, 4, 2, 128, [0, 7, 40], [0, 9, 0]),             # empty chunks
+    (2, 16, 2, 64, [511, 2], [600, 513]),              # several query tiles each
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"case{i}" for i in range(len(CASES))])
+def test_append_then_paged_prefill(case):
+    B, Hq, Hkv, d, P, c = case
+    x = wl.chunked_prefill_inputs(B, Hq, Hkv, d, P, c, seed=600 + sum(c), permute=True)
+    wl.poison_chunk_slots(x)
+    log(f"case: B={B} Hq={Hq} Hkv={Hkv} d={d} prefix={P} chunk={c}")
+    got, lse, kp, vp = gpu_chunk(x)
+    ref_kp, ref_vp = ao.kv_append_ref(x.k_pages, x.v_pages, x.block_table, x.k_new, x.v_new,
+                                      x.cu_q, x.prefix_lens)
+    assert torch.equal(bits(kp), bits(ref_kp)) and torch.equal(bits(vp), bits(ref_vp))
+    if x.total_q == 0:
+        return
+    ref, ref_lse = ao.paged_prefill_ref(x.q, ref_kp, ref_vp, x.block_table, x.cu_q, x.seq_lens, x.scale)
+    e = np.abs(got.double().numpy() - ref)
+    log(f"  max-abs {e.max():.3e} mean-abs {e.mean():.3e}")
+    assert e.max() <= BF16_MAX and e.mean() <= BF16_MEAN
+    assert np.abs(lse.double().numpy() - ref_lse).max() <= LSE_BF16
+
+
+def test_append_leaves_other_slots_and_writes_exact_rows():
+    x = wl.chunked_prefill_inputs(3, 2, 8, 128, [3, 0, 47], [20, 5, 33], seed=651)
+    kp, vp, _, _ = gpu_append(x)
+    torch.cuda.synchronize()
+    ref_kp, ref_vp = ao.kv_append_ref(x.k_pages, x.v_pages, x.block_table, x.k_new, x.v_new,
+                                      x.cu_q, x.prefix_lens)
+    assert torch.equal(bits(kp.cpu()), bits(ref_kp)) and torch.equal(bits(vp.cpu()), bits(ref_vp))
+
+
+@pytest.mark.parametrize("d,Hkv", [(128, 2), (64, 4)])
+def test_no_prefix_is_bit_identical_to_contiguous_prefill(d, Hkv):
+    N = 320
+    x = wl.prefill_inputs(1, N, 8, Hkv, d, seed=660 + d)
+    o_ref = bd.attn_prefill_ex(x.q.cuda(), x.k.cuda(), x.v.cuda(), scale=x.scale)
+    kp = x.k[0].reshape(N // 16, 16, Hkv, d).contiguous().cuda()
+    vp = x.v[0].reshape(N // 16, 16, Hkv, d).contiguous().cuda()
+    table = torch.arange(N // 16, dtype=torch.int32).reshape(1, -1).cuda()
+    cu = torch.tensor([0, N], dtype=torch.int32).cuda()
+    lens = torch.tensor([N], dtype=torch.int32).cuda()
+    o = bd.attn_prefill_paged(x.q[0].contiguous().cuda(), kp, vp, table, cu, lens, scale=x.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(o.cpu()), bits(o_ref[0].cpu()))
+
+
+def test_chunks_reproduce_a_whole_prompt():
+    """A prompt run as three chunks (append, then attend, per chunk) gives the
+    rows a single causal prefill of the whole prompt gives, to the tolerance."""
+    B, N, Hq, Hkv, d = 2, 700, 8, 2, 128
+    x = wl.prefill_inputs(B, N, Hq, Hkv, d, seed=670)
+    n_pages = B * (-(-N // 16))
+    kp = torch.full((n_pages, 16, Hkv, d), float("nan"), dtype=torch.bfloat16).cuda()
+    vp = torch.full_like(kp, float("nan"))
+    perm = torch.randperm(n_pages, generator=torch.Generator().manual_seed(671)).to(torch.int32)
+    table = perm.reshape(B, -1).cuda()
+    outs = []
+    for s0, s1 in ((0, 300), (300, 301), (301, N)):
+        c = s1 - s0
+        cu = torch.tensor([0, c, 2 * c], dtype=torch.int32).cuda()
+        start = torch.tensor([s0, s0], dtype=torch.int32).cuda()
+        kn = x.k[:, s0:s1].reshape(B * c, Hkv, d).contiguous().cuda()
+        vn = x.v[:, s0:s1].reshape(B * c, Hkv, d).contiguous().cuda()
+        bd.attn_kv_append(kn, vn, kp, vp, table, cu, start)
+        q = x.q[:, s0:s1].reshape(B * c, Hq, d).contiguous().cuda()
+        lens = torch.tensor([s1, s1], dtype=torch.int32).cuda()
+        outs.append(bd.attn_prefill_paged(q, kp, vp, table, cu, lens, scale=x.scale).cpu().reshape(B, c, Hq, d))
+    torch.cuda.synchronize()
+    got = torch.cat(outs, dim=1)
+    ref, _ = ao.sdpa_ref(ao.to_bhnd(x.q, "BNHD"), ao.to_bhnd(x.k, "BNHD"), ao.to_bhnd(x.v, "BNHD"), x.scale)
+    e = np.abs(got.double().numpy() - ao.from_bhnd(ref, "BNHD"))
+    log(f"  max-abs {e.max():.3e} mean-abs {e.mean():.3e}")
+    assert e.max() <= BF16_MAX and e.mean() <= BF16_MEAN
+
+
+def test_workload_6_full_size_sampled():
+    x = wl.workload_6()
+    log(f"case: {x.name} (T={x.total_q}, seq_lens={x.seq_lens.tolist()})")
+    got, lse, kp, vp = gpu_chunk(x)
+    ref_kp, ref_vp = ao.kv_append_ref(x.k_pages, x.v_pages, x.block_table, x.k_new, x.v_new,
+                                      x.cu_q, x.prefix_lens)
+    assert torch.equal(bits(kp), bits(ref_kp)) and torch.equal(bits(vp), bits(ref_vp))
+    rng = np.random.default_rng(680)
+    worst = 0.0
+    for b in range(x.B):
+        L, P = int(x.seq_lens[b]), int(x.prefix_lens[b])
+        K = ao.gather_kv_ref(ref_kp.float().numpy(), x.block_table[b].numpy(), L, x.page_size)
+        V = ao.gather_kv_ref(ref_vp.float().numpy(), x.block_table[b].numpy(), L, x.page_size)
+        c = L - P
+        rows = [0, c - 1] + rng.integers(0, c, 4).tolist()
+        for i in rows:
+            h = int(rng.integers(0, x.Hq))
+            kv = ao.kv_head_of(h, x.Hq, x.Hkv)
+            r = int(x.cu_q[b]) + i
+            allowed = ao.position_mask([P + i], np.arange(L))
+            o, l = ao.sdpa_masked_ref(x.q[r, h][None, None], K[None, :, kv], V[None, :, kv], x.scale, allowed)
+            e = np.abs(got[r, h].double().numpy() - o[0, 0]).max()
+            worst = max(worst, e)
+            assert e <= BF16_MAX, (b, i, h, e)
+            assert abs(float(lse[h, r]) - l[0, 0]) <= LSE_BF16
+    log(f"  sampled max-abs {worst:.3e}")
