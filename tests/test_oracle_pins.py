@@ -392,6 +392,128 @@ def test_append_writes_only_its_slots_and_gathers_back():
     assert torch.equal(kq, kp) and torch.equal(vq, vp)
 
 
+# ------------------------------------------------------------ window and sink variants
+
+def test_window_mask_matches_printed_grid():
+    lines = list(golden_lines("window_mask.txt"))
+    W = int(lines[0].split()[1])
+    grid = np.array([[int(c) for c in l.split()] for l in lines[1:]], dtype=bool)
+    n = grid.shape[0]
+    assert np.array_equal(ao.position_mask(np.arange(n), np.arange(n), W), grid)
+    # a window as long as the sequence is plain causality
+    assert np.array_equal(ao.position_mask(np.arange(n), np.arange(n), n), np.tril(np.ones((n, n), bool)))
+
+
+def test_initial_tokens_stay_visible_with_a_window():
+    n, W, S = 9, 3, 2
+    got = ao.position_mask(np.arange(n), np.arange(n), W, S)
+    tri = np.tril(np.ones((n, n), bool))
+    band = np.triu(tri, -(W - 1))               # 0 <= i - j < W
+    anchors = tri & (np.arange(n)[None, :] < S)
+    assert np.array_equal(got, band | anchors)
+    with pytest.raises(ValueError):
+        ao.position_mask(np.arange(3), np.arange(3), None, 1)
+
+
+def test_sink_mass_matches_printed_closed_form():
+    n_checked = 0
+    for line in golden_lines("sink_mass.txt"):
+        n, s, pct = line.split()
+        n, s, pct = int(n), float(s), float(pct)
+        q = np.zeros((1, 1, 4))
+        k = rnd((1, n, 4), 7)
+        v = np.ones((1, n, 4))
+        o, lse = ao.sdpa_masked_ref(q, k, v, 0.5, np.ones((1, n), bool), sinks=[s])
+        p_sink = 1.0 - o[0, 0, 0]            # the sink takes mass but adds no value
+        assert abs(p_sink - math.exp(s) / (n + math.exp(s))) <= 1e-12
+        assert abs(100 * p_sink - pct) <= 0.005
+        assert abs(lse[0, 0] - math.log(n + math.exp(s))) <= 1e-12
+        n_checked += 1
+    assert n_checked == 3
+
+
+def test_sink_equals_an_extra_constant_coordinate_key_with_zero_value():
+    """The page's exact abstraction: a score slot with zero value, written as
+    a dot product by extending q with a constant coordinate."""
+    Hq, Hkv, N, d, scale = 4, 2, 11, 6, 0.37
+    q, k, v = rnd((Hq, N, d), 130), rnd((Hkv, N, d), 131), rnd((Hkv, N, d), 132)
+    sinks = np.array([0.3, -1.0, 2.5, 0.0])
+    allowed = ao.position_mask(np.arange(N), np.arange(N), 5)
+    o, lse = ao.sdpa_masked_ref(q, k, v, scale, allowed, sinks)
+    g = Hq // Hkv
+    for h in range(Hq):
+        qe = np.concatenate([q[h], np.ones((N, 1))], axis=1)              # [N, d+1]
+        ke = np.concatenate([k[h // g], np.zeros((N, 1))], axis=1)
+        ks = np.concatenate([np.zeros((1, d)), [[sinks[h] / scale]]], axis=1)
+        ke = np.concatenate([ke, ks])                                       # sink key last
+        ve = np.concatenate([v[h // g], np.zeros((1, d))])
+        m = np.concatenate([allowed, np.ones((N, 1), bool)], axis=1)
+        want = F.scaled_dot_product_attention(torch.from_numpy(qe)[None], torch.from_numpy(ke)[None],
+                                              torch.from_numpy(ve)[None], attn_mask=torch.from_numpy(m),
+                                              scale=scale)[0].numpy()
+        assert np.abs(o[h] - want).max() <= 1e-12
+        sc = (qe @ ke.T) * scale
+        sc[~m] = -np.inf
+        assert np.abs(lse[h] - torch.logsumexp(torch.from_numpy(sc), -1).numpy()).max() <= 1e-12
+
+
+def test_shifting_token_logits_but_not_the_sink_changes_the_output():
+    q, k, v = rnd((1, 1, 4), 140), rnd((1, 7, 4), 141), rnd((1, 7, 4), 142)
+    allowed = np.ones((1, 7), bool)
+    a, _ = ao.sdpa_masked_ref(q, k, v, 1.0, allowed, sinks=[0.5])
+    # adding c to every token score = adding c * q / |q|^2 to every key
+    shift = q[0, 0] / (q[0, 0] @ q[0, 0]) * 1.5
+    b, _ = ao.sdpa_masked_ref(q, k + shift, v, 1.0, allowed, sinks=[0.5])
+    c, _ = ao.sdpa_masked_ref(q, k + shift, v, 1.0, allowed, sinks=[2.0])
+    assert np.abs(a - b).max() > 1e-3        # the sink stayed put: different output
+    assert np.abs(a - c).max() <= 1e-12      # shifting the sink too: softmax shift invariance
+
+
+@pytest.mark.parametrize("W,S", [(1, 0), (4, 0), (7, 2), (64, 0)])
+def test_windowed_prefill_matches_torch_with_explicit_mask(W, S):
+    B, Hq, Hkv, N, d = 2, 4, 2, 23, 8
+    q, k, v = rnd((B, N, Hq, d), 150), rnd((B, N, Hkv, d), 151), rnd((B, N, Hkv, d), 152)
+    o, lse = ao.prefill_variant_ref(q, k, v, 0.3, "BNHD", window=W, n_sink=S)
+    i, j = np.arange(N)[:, None], np.arange(N)[None, :]
+    m = torch.from_numpy(((j <= i) & (i - j < W)) | ((j <= i) & (j < S)))
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a.transpose(0, 2, 1, 3)))
+    want = F.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=m, scale=0.3,
+                                          enable_gqa=True).numpy().transpose(0, 2, 1, 3)
+    assert np.abs(o - want).max() <= 1e-12
+
+
+def test_windowed_chunk_rows_equal_the_tail_of_a_windowed_prefill():
+    from exact_attention_flashattention_amd import workloads as wl
+    x = wl.chunked_prefill_inputs(1, 4, 2, 8, [13], [9], seed=170, dtype=torch.float32, page_size=4)
+    kp, vp = ao.kv_append_ref(x.k_pages, x.v_pages, x.block_table, x.k_new, x.v_new, x.cu_q, x.prefix_lens)
+    L = int(x.seq_lens[0])
+    K = ao.gather_kv_ref(kp.numpy(), x.block_table[0].numpy(), L, 4)
+    V = ao.gather_kv_ref(vp.numpy(), x.block_table[0].numpy(), L, 4)
+    sinks = np.array([0.5, -0.5, 1.5, 0.0])
+    for W, S in [(3, 0), (6, 2)]:
+        o, lse = ao.paged_prefill_ref(x.q, kp, vp, x.block_table, x.cu_q, x.seq_lens, 0.35,
+                                      window=W, n_sink=S, sinks=sinks)
+        qfull = np.concatenate([rnd((13, 4, 8), 171), x.q.double().numpy()])[None]
+        full, full_lse = ao.prefill_variant_ref(qfull, K[None], V[None], 0.35, "BNHD", window=W,
+                                                n_sink=S, sinks=sinks)
+        assert np.abs(o - full[0, 13:]).max() <= 1e-12
+        assert np.abs(lse - full_lse[0, :, 13:]).max() <= 1e-12
+
+
+def test_windowed_decode_is_the_last_row_of_the_windowed_prefill():
+    B, Hq, Hkv, N, d, ps = 2, 4, 2, 21, 8, 4
+    q, k, v = rnd((B, Hq, N, d), 160), rnd((B, Hkv, N, d), 161), rnd((B, Hkv, N, d), 162)
+    sinks = np.array([0.1, 1.0, -2.0, 3.0])
+    for W, S in [(5, 0), (5, 3), (100, 0)]:
+        o, _ = ao.prefill_variant_ref(q, k, v, 0.4, "BHND", window=W, n_sink=S, sinks=sinks)
+        for t in (0, 6, 20):
+            lens = [t + 1] * B
+            kp, vp, table = _paged_copy(k, v, lens, ps, seed=t)
+            dec = ao.decode_ref(q[:, :, t], kp, vp, table, np.array(lens), 0.4, window=W, n_sink=S,
+                                sinks=sinks)
+            assert np.abs(dec - o[:, :, t]).max() <= 1e-12
+
+
 # ------------------------------------------------------------ cache sizing
 
 def test_kv_cache_bytes_matches_printed_values():
