@@ -17,7 +17,11 @@ Outside the timed step, "chunked_prefill" reports the chunked-prefill pair
 on its own workload (bf16, B=4, Hq=32, Hkv=8, d=128, a 2048-token chunk after
 a cached prefix of U[6144, 14336] tokens, permuted 16-token pages): the KV
 append in GB/s (new K/V rows read once and written once) and the paged
-prefill in TFLOP/s (visible (query, key) pairs, 4 d flops each).
+prefill in TFLOP/s (visible (query, key) pairs, 4 d flops each). "variants"
+reports the headline prefill with a 1024-token window, 4 initial tokens and
+per-head sink logits (TFLOP/s over the visible pairs), and the long-context
+decode with an 8192-token window, 4 initial tokens and sink logits (GB/s over
+the K/V bytes of the visible tokens).
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -181,6 +185,62 @@ def chunked_report(dev, stream, steps: int) -> dict:
     }
 
 
+def window_pairs(N: int, W: int, n_sink: int = 0) -> int:
+    """Visible (query, key) pairs of causal self-attention with a window W
+    and n_sink initial positions kept: row i sees min(i+1, W) window keys
+    plus the anchors before its window."""
+    pairs = 0
+    for i in range(N):
+        lo = max(i - W + 1, 0)
+        pairs += (i + 1 - lo) + min(n_sink, lo)
+    return pairs
+
+
+def variants_report(dev, stream, steps: int) -> dict:
+    """Sliding window + initial tokens + learned sink logits on the headline
+    prefill shape and the long-context decode, timed apart from the step."""
+    import torch
+    import exact_attention_flashattention_amd as pkg
+    from exact_attention_flashattention_amd import workloads as wl
+    W, S = 1024, 4
+    x2 = wl.workload_2()
+    q, k, v = x2.q.to(dev), x2.k.to(dev), x2.v.to(dev)
+    o = torch.empty_like(q)
+    sinks = torch.linspace(-1.0, 3.0, x2.Hq, device=dev, dtype=torch.float32)
+    pre = lambda: pkg.attn_prefill_ex(q, k, v, o, scale=x2.scale, window=W, n_sink=S, sinks=sinks,
+                                      stream=stream)
+    t_pre = time_calls(pre, stream, 3, steps)
+    fl = 4 * x2.B * x2.Hq * x2.d * window_pairs(x2.N, W, S)
+    tf = fl / (t_pre * 1e-6) / 1e12
+    del q, k, v, o
+    x5 = wl.workload_5()
+    Wd = 8192
+    t = [a.to(dev) for a in (x5.q, x5.k_pages, x5.v_pages, x5.block_table, x5.seq_lens)]
+    do = torch.empty_like(t[0])
+    dsinks = torch.linspace(-1.0, 3.0, x5.Hq, device=dev, dtype=torch.float32)
+    ws = torch.empty(pkg.attn_decode_workspace_size(x5.B, x5.Hq, x5.Hkv, x5.d, x5.max_pages_per_seq, 0) // 4 + 4,
+                     dtype=torch.float32, device=dev)
+    dec = lambda: pkg.attn_decode_ex(*t, do, scale=x5.scale, window=Wd, n_sink=S, sinks=dsinks, workspace=ws,
+                                     stream=stream)
+    t_dec = time_calls(dec, stream, 3, steps)
+    # K+V bytes of the visible tokens (window + anchors) once
+    vis = sum(min(int(L), Wd) + min(S, max(int(L) - Wd, 0)) for L in x5.seq_lens.tolist())
+    by = vis * x5.Hkv * x5.d * 2 * 2
+    gb = by / (t_dec * 1e-6) / 1e9
+    log(f"variants: windowed prefill {t_pre:.1f} us ({tf:.1f} TFLOP/s), windowed decode {t_dec:.1f} us "
+        f"({gb:.0f} GB/s)")
+    return {
+        "prefill": {"workload": f"{x2.name} window={W} n_sink={S} sinks=per-head", "value": round(tf, 3),
+                    "unit": "TFLOP/s", "avg_launch_us": round(t_pre, 2), "flops_per_launch": fl,
+                    "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4)}},
+        "decode": {"workload": f"{x5.name} window={Wd} n_sink={S} sinks=per-head", "value": round(gb, 2),
+                   "unit": "GB/s", "avg_call_us": round(t_dec, 2), "kv_bytes_per_call": by,
+                   "roofline": {"bound": "hbm", "achieved": round(gb, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(gb / HBM_PEAK_GBS, 4)}},
+    }
+
+
 PREFILL_SOURCES = ["prefill_bf16.hip", "attn_internal.h"]
 DECODE_SOURCES = ["decode.hip", "attn_internal.h"]
 
@@ -292,7 +352,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-chunked", action="store_true",
-                    help="skip the chunked-prefill (KV append + paged prefill) report")
+                    help="skip the chunked-prefill (KV append + paged prefill) and variant reports")
     ap.add_argument("--cpu-batches", type=int, default=2,
                     help="batch entries of the headline prefill the CPU oracle is timed on")
     ap.add_argument("--only", choices=["prefill", "decode", "copy", "chunked", "append"], default=None,
@@ -411,10 +471,12 @@ def main() -> int:
                          "kernel": "decode_split_kernel<128> + decode_merge_kernel<128>"},
         },
         "chunked_prefill": None,
+        "variants": None,
         "cpu_baseline": None,
     }
     if not args.no_chunked:
         result["chunked_prefill"] = chunked_report(dev, stream, max(10, args.steps // 2))
+        result["variants"] = variants_report(dev, stream, max(10, args.steps // 2))
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(x2, x5, args.cpu_batches)

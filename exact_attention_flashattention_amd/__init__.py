@@ -6,7 +6,7 @@ this package only marshals torch GPU tensors into those calls. Nothing here
 computes attention on the CPU.
 """
 from .binding import (  # noqa: F401
-    AttnError, AttnLibraryMissing, LIB_PATH, attn_decode, attn_decode_num_splits,
+    AttnError, AttnLibraryMissing, AttnVariant, LIB_PATH, attn_decode, attn_decode_ex, attn_decode_num_splits,
     attn_decode_workspace_size, attn_gather_pages, attn_kv_append, attn_prefill, attn_prefill_ex,
     attn_prefill_paged, attn_status_string, lib,
 )

@@ -19,17 +19,26 @@ ATTN_F32, ATTN_BF16 = 0, 1
 ATTN_BNHD, ATTN_BHND = 0, 1
 LAYOUTS = {"BNHD": ATTN_BNHD, "BHND": ATTN_BHND}
 
+class AttnVariant(ctypes.Structure):
+    """struct attn_variant: window (0 = none), n_sink initial positions kept
+    visible with a window, sinks = device fp32 [Hq] sink logits or NULL."""
+    _fields_ = [("window", ctypes.c_int), ("n_sink", ctypes.c_int), ("sinks", ctypes.c_void_p)]
+
+
 # (name, restype, argtypes) for every symbol declared in include/attn.h
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_var = ctypes.POINTER(AttnVariant)
 SIGNATURES = [
     ("attn_prefill", _i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]),
-    ("attn_prefill_ex", _i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _i, _vp]),
+    ("attn_prefill_ex", _i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _i, _var, _vp]),
     ("attn_decode_num_splits", _i, [_i, _i, _i, _i]),
     ("attn_decode_workspace_size", _sz, [_i, _i, _i, _i, _i, _i]),
     ("attn_decode", _i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    ("attn_decode_ex", _i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _var, _vp,
+                            _sz, _vp]),
     ("attn_kv_append", _i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
     ("attn_prefill_paged", _i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
-                                _i, _i, _f, _vp]),
+                                _i, _i, _f, _var, _vp]),
     ("attn_gather_pages", _i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
     ("attn_status_string", ctypes.c_char_p, [_i]),
     ("attn_version", _i, []),
@@ -92,10 +101,27 @@ def _dev(t, name):
     return t.data_ptr()
 
 
+def _variant(window: int, n_sink: int, sinks, Hq: int):
+    """A pointer to an attn_variant, or None when no variant is asked for.
+    The struct is returned with the pointer so it outlives the call."""
+    import torch
+    if not window and not n_sink and sinks is None:
+        return None, None
+    ptr = None
+    if sinks is not None:
+        if sinks.dtype != torch.float32 or tuple(sinks.shape) != (Hq,):
+            raise ValueError("sinks must be float32 [Hq]")
+        ptr = _dev(sinks, "sinks")
+    v = AttnVariant(int(window), int(n_sink), ptr)
+    return ctypes.pointer(v), v
+
+
 def attn_prefill_ex(q, k, v, o=None, *, causal: bool = True, scale: Optional[float] = None,
-                    layout: str = "BNHD", lse=None, stream=None):
+                    layout: str = "BNHD", lse=None, window: int = 0, n_sink: int = 0, sinks=None,
+                    stream=None):
     """Causal (or full) GQA attention. q [B,N,Hq,d] / [B,Hq,N,d] and k, v with
-    Hkv heads, bf16 or fp32 (all alike). Returns o (allocated if not given)."""
+    Hkv heads, bf16 or fp32 (all alike). window / n_sink / sinks select the
+    attn_variant options (bf16 only). Returns o (allocated if not given)."""
     import torch
     if layout not in LAYOUTS:
         raise ValueError(f"layout must be one of {list(LAYOUTS)}")
@@ -127,9 +153,10 @@ def attn_prefill_ex(q, k, v, o=None, *, causal: bool = True, scale: Optional[flo
         if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N):
             raise ValueError("lse must be float32 [B, Hq, N]")
         lse_ptr = _dev(lse, "lse")
+    var, _keep = _variant(window, n_sink, sinks, Hq)
     st = lib().attn_prefill_ex(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), lse_ptr,
                                B, N, Hq, Hkv, d, float(scale), int(bool(causal)), dtype,
-                               LAYOUTS[layout], _stream(stream))
+                               LAYOUTS[layout], var, _stream(stream))
     _check(st, "attn_prefill_ex")
     return o
 
@@ -166,6 +193,19 @@ def attn_decode(q, k_pages, v_pages, block_table, seq_lens, o=None, *, scale: Op
                 num_splits: int = 0, workspace=None, stream=None):
     """Paged decode. q [B,Hq,d] bf16; pools [num_pages,16,Hkv,d] bf16;
     block_table int32 [B,max_pages]; seq_lens int32 [B]. Returns o [B,Hq,d]."""
+    return _decode(q, k_pages, v_pages, block_table, seq_lens, o, scale, num_splits, workspace,
+                   stream, None)
+
+
+def attn_decode_ex(q, k_pages, v_pages, block_table, seq_lens, o=None, *, scale: Optional[float] = None,
+                   num_splits: int = 0, window: int = 0, n_sink: int = 0, sinks=None, workspace=None,
+                   stream=None):
+    """attn_decode with the attn_variant options (window, n_sink, sinks)."""
+    return _decode(q, k_pages, v_pages, block_table, seq_lens, o, scale, num_splits, workspace,
+                   stream, (window, n_sink, sinks))
+
+
+def _decode(q, k_pages, v_pages, block_table, seq_lens, o, scale, num_splits, workspace, stream, variant):
     import torch
     if q.dtype != torch.bfloat16 or k_pages.dtype != torch.bfloat16 or v_pages.dtype != torch.bfloat16:
         raise ValueError("decode takes bf16 q and pools")
@@ -184,12 +224,18 @@ def attn_decode(q, k_pages, v_pages, block_table, seq_lens, o=None, *, scale: Op
     if workspace is None:
         workspace = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib().attn_decode(_dev(q, "q"), _dev(k_pages, "k_pages"), _dev(v_pages, "v_pages"),
-                           _dev(block_table, "block_table"), _dev(seq_lens, "seq_lens"), _dev(o, "o"),
-                           B, Hq, Hkv, d, page_size, mpps, num_pages,
-                           float(d ** -0.5 if scale is None else scale), num_splits,
-                           _dev(workspace, "workspace"), ws_bytes, _stream(stream))
-    _check(st, "attn_decode")
+    args = (_dev(q, "q"), _dev(k_pages, "k_pages"), _dev(v_pages, "v_pages"),
+            _dev(block_table, "block_table"), _dev(seq_lens, "seq_lens"), _dev(o, "o"),
+            B, Hq, Hkv, d, page_size, mpps, num_pages, float(d ** -0.5 if scale is None else scale),
+            num_splits)
+    tail = (_dev(workspace, "workspace"), ws_bytes, _stream(stream))
+    if variant is None:
+        st = lib().attn_decode(*args, *tail)
+        _check(st, "attn_decode")
+    else:
+        var, _keep = _variant(*variant, Hq)
+        st = lib().attn_decode_ex(*args, var, *tail)
+        _check(st, "attn_decode_ex")
     return o
 
 
@@ -229,7 +275,7 @@ def attn_kv_append(k_new, v_new, k_pages, v_pages, block_table, cu_new, start_po
 
 def attn_prefill_paged(q, k_pages, v_pages, block_table, cu_q, seq_lens, o=None, *,
                        max_q_len: Optional[int] = None, scale: Optional[float] = None, lse=None,
-                       stream=None):
+                       window: int = 0, n_sink: int = 0, sinks=None, stream=None):
     """Chunk queries q [T, Hq, d] bf16 (sequence b owns rows cu_q[b] ..
     cu_q[b+1]-1, at positions seq_lens[b] - c_b ..) against the paged cache.
     Returns o [T, Hq, d]; lse, if given, is float32 [Hq, T]. max_q_len
@@ -256,11 +302,12 @@ def attn_prefill_paged(q, k_pages, v_pages, block_table, cu_q, seq_lens, o=None,
         if lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, T):
             raise ValueError("lse must be float32 [Hq, T]")
         lse_ptr = _dev(lse, "lse")
+    var, _keep = _variant(window, n_sink, sinks, Hq)
     st = lib().attn_prefill_paged(_dev(q, "q"), _dev(k_pages, "k_pages"), _dev(v_pages, "v_pages"),
                                   _dev(block_table, "block_table"), _dev(cu_q, "cu_q"),
                                   _dev(seq_lens, "seq_lens"), _dev(o, "o"), lse_ptr, B, Hq, Hkv, d,
                                   page_size, block_table.shape[1], num_pages, T, max_q_len,
-                                  float(d ** -0.5 if scale is None else scale), _stream(stream))
+                                  float(d ** -0.5 if scale is None else scale), var, _stream(stream))
     _check(st, "attn_prefill_paged")
     return o
 

@@ -19,6 +19,25 @@ int check_heads(int Hq, int Hkv) {
   return ATTN_OK;
 }
 
+// A variant: window >= 0, n_sink >= 0 only with a window, a window only when
+// causal, the sink array 4-byte aligned.
+int check_variant(const attn_variant* v, int causal) {
+  if (!v) return ATTN_OK;
+  if (v->window < 0 || v->n_sink < 0) return ATTN_ERR_SHAPE;
+  if (v->n_sink > 0 && v->window == 0) return ATTN_ERR_SHAPE;
+  if (v->window > 0 && !causal) return ATTN_ERR_SHAPE;
+  if (v->sinks && (reinterpret_cast<uintptr_t>(v->sinks) & 3u)) return ATTN_ERR_ALIGN;
+  return ATTN_OK;
+}
+
+bool has_variant(const attn_variant* v) { return v && (v->window > 0 || v->sinks); }
+
+void set_variant(attn::PrefillParams& p, const attn_variant* v) {
+  p.window = v ? v->window : 0;
+  p.n_sink = v && v->window > 0 ? v->n_sink : 0;
+  p.sinks = v ? v->sinks : nullptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -44,7 +63,7 @@ const char* attn_status_string(int status) {
 
 int attn_prefill_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                     int B, int N, int Hq, int Hkv, int d, float scale, int causal,
-                    int dtype, int layout, void* stream) {
+                    int dtype, int layout, const attn_variant* variant, void* stream) {
   if (!q || !k || !v || !o) return ATTN_ERR_NULL;
   if (B < 1 || N < 1) return ATTN_ERR_SHAPE;
   int st = check_heads(Hq, Hkv);
@@ -58,6 +77,9 @@ int attn_prefill_ex(const void* q, const void* k, const void* v, void* o, float*
   if (dtype == ATTN_F32 && (Hq > 65535 || B > 65535)) return ATTN_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_ALIGN;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return ATTN_ERR_ALIGN;
+  st = check_variant(variant, causal);
+  if (st) return st;
+  if (has_variant(variant) && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
 
   attn::PrefillParams p = {};
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
@@ -73,6 +95,7 @@ int attn_prefill_ex(const void* q, const void* k, const void* v, void* o, float*
   p.o_sb = p.q_sb; p.o_sn = p.q_sn; p.o_sh = p.q_sh;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.causal = causal ? 1 : 0;
+  set_variant(p, variant);
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const hipError_t e = dtype == ATTN_BF16 ? attn::launch_prefill_bf16(p, d, s)
@@ -83,7 +106,7 @@ int attn_prefill_ex(const void* q, const void* k, const void* v, void* o, float*
 int attn_prefill(const void* q, const void* k, const void* v, void* o,
                  int B, int N, int Hq, int Hkv, int d, float scale, int causal, void* stream) {
   return attn_prefill_ex(q, k, v, o, nullptr, B, N, Hq, Hkv, d, scale, causal, ATTN_BF16,
-                         ATTN_BNHD, stream);
+                         ATTN_BNHD, nullptr, stream);
 }
 
 int attn_decode_num_splits(int B, int Hkv, int max_pages_per_seq, int num_splits) {
@@ -103,11 +126,11 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int d, int max_pages_p
   return (size_t)B * Hq * S * (d + 2) * sizeof(float);
 }
 
-int attn_decode(const void* q, const void* k_pages, const void* v_pages,
-                const int32_t* block_table, const int32_t* seq_lens, void* o,
-                int B, int Hq, int Hkv, int d, int page_size, int max_pages_per_seq,
-                int num_pages, float scale, int num_splits,
-                void* workspace, size_t workspace_bytes, void* stream) {
+int attn_decode_ex(const void* q, const void* k_pages, const void* v_pages,
+                   const int32_t* block_table, const int32_t* seq_lens, void* o,
+                   int B, int Hq, int Hkv, int d, int page_size, int max_pages_per_seq,
+                   int num_pages, float scale, int num_splits, const attn_variant* variant,
+                   void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !o) return ATTN_ERR_NULL;
   if (B < 1 || max_pages_per_seq < 1 || num_pages < 1 || num_splits < 0) return ATTN_ERR_SHAPE;
   int st = check_heads(Hq, Hkv);
@@ -125,8 +148,10 @@ int attn_decode(const void* q, const void* k_pages, const void* v_pages,
       !aligned16(workspace) || (reinterpret_cast<uintptr_t>(block_table) & 3u) ||
       (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
     return ATTN_ERR_ALIGN;
+  st = check_variant(variant, 1);
+  if (st) return st;
 
-  attn::DecodeParams p;
+  attn::DecodeParams p = {};
   p.q = q; p.k_pages = k_pages; p.v_pages = v_pages;
   p.block_table = block_table; p.seq_lens = seq_lens; p.o = o;
   p.ws_o = static_cast<float*>(workspace);
@@ -134,8 +159,21 @@ int attn_decode(const void* q, const void* k_pages, const void* v_pages,
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.max_pages_per_seq = max_pages_per_seq;
   p.num_splits = S;
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.window = variant ? variant->window : 0;
+  p.n_sink = variant && variant->window > 0 ? variant->n_sink : 0;
+  p.sinks = variant ? variant->sinks : nullptr;
   const hipError_t e = attn::launch_decode(p, d, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_decode(const void* q, const void* k_pages, const void* v_pages,
+                const int32_t* block_table, const int32_t* seq_lens, void* o,
+                int B, int Hq, int Hkv, int d, int page_size, int max_pages_per_seq,
+                int num_pages, float scale, int num_splits,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_decode_ex(q, k_pages, v_pages, block_table, seq_lens, o, B, Hq, Hkv, d, page_size,
+                        max_pages_per_seq, num_pages, scale, num_splits, nullptr, workspace,
+                        workspace_bytes, stream);
 }
 
 int attn_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
@@ -167,7 +205,7 @@ int attn_prefill_paged(const void* q, const void* k_pages, const void* v_pages,
                        const int32_t* block_table, const int32_t* cu_q, const int32_t* seq_lens,
                        void* o, float* lse, int B, int Hq, int Hkv, int d, int page_size,
                        int max_pages_per_seq, int num_pages, int total_q, int max_q_len,
-                       float scale, void* stream) {
+                       float scale, const attn_variant* variant, void* stream) {
   if (!q || !k_pages || !v_pages || !block_table || !cu_q || !seq_lens || !o) return ATTN_ERR_NULL;
   if (B < 1 || max_pages_per_seq < 1 || num_pages < 1 || total_q < 0 || max_q_len < 0)
     return ATTN_ERR_SHAPE;
@@ -184,6 +222,8 @@ int attn_prefill_paged(const void* q, const void* k_pages, const void* v_pages,
       (reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(cu_q) & 3u) ||
       (reinterpret_cast<uintptr_t>(seq_lens) & 3u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
     return ATTN_ERR_ALIGN;
+  st = check_variant(variant, 1);
+  if (st) return st;
   if (total_q == 0 || max_q_len == 0) return ATTN_OK;  // no query rows
 
   attn::PrefillParams p = {};
@@ -197,6 +237,7 @@ int attn_prefill_paged(const void* q, const void* k_pages, const void* v_pages,
   p.cu_q = cu_q; p.seq_lens = seq_lens; p.block_table = block_table;
   p.max_pages_per_seq = max_pages_per_seq;
   p.total_q = total_q;
+  set_variant(p, variant);
   const hipError_t e = attn::launch_prefill_paged(p, d, max_q_len, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }

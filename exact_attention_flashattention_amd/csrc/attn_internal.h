@@ -29,6 +29,12 @@ struct PrefillParams {
   const int32_t* block_table;
   int max_pages_per_seq;
   int total_q;  // lse layout [Hq, total_q]
+  // Variants (causal only): window W > 0 keeps keys with 0 <= p_q - p_k < W,
+  // plus the first n_sink positions; sinks (fp32 [Hq] or null) is a learned
+  // logit per query head with zero value.
+  int window;
+  int n_sink;
+  const float* sinks;
 };
 
 // One decode problem (bf16 pages, page_size 16).
@@ -43,6 +49,11 @@ struct DecodeParams {
   float* ws_o;                 // [B, Hq, splits, d]   unnormalised partial outputs
   int B, Hq, Hkv, max_pages_per_seq, num_splits;
   float scale_log2;
+  // Variants: window W > 0 keeps tokens t >= L - W plus t < n_sink; sinks
+  // (fp32 [Hq] or null) is a learned logit per query head with zero value.
+  int window;
+  int n_sink;
+  const float* sinks;
 };
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream);

@@ -122,11 +122,23 @@ __global__ __launch_bounds__(NWU * 64, ATTN_DECODE_WAVES_PER_SIMD) void decode_s
   const bool head_ok = head_local < g;
   const int h = kvh * g + head_local;
 
+  // Visited logical pages: [0, np) or, with a window W, the pages holding the
+  // n_sink initial positions, [0, sp), then the window's pages, [wp0, np).
+  // The splits cut the visited pages (numbered 0 .. nv-1) into ranges.
   const int L = p.seq_lens[b];
   const int np = (L + PAGE - 1) / PAGE;
-  const int pps = (np + S - 1) / S;
-  const int pg_begin = min(np, split * pps);
-  const int pg_end = min(np, pg_begin + pps);
+  int sp = 0, wp0 = 0;
+  if (p.window > 0) {
+    wp0 = max(L - p.window, 0) / PAGE;
+    sp = min((p.n_sink + PAGE - 1) / PAGE, wp0);
+  }
+  const int nv = sp + (np - wp0);
+  const int pps = (nv + S - 1) / S;
+  const int v_begin = min(nv, split * pps);
+  const int v_end = min(nv, v_begin + pps);
+  auto page_of = [&](int vi) { return vi < sp ? vi : wp0 + (vi - sp); };
+  // token t is visible iff t < L and (t >= lo_t or t < n_sink)
+  const int lo_t = p.window > 0 ? L - p.window : 0;
 
   const __bf16* __restrict__ kp = (const __bf16*)p.k_pages;
   const __bf16* __restrict__ vp = (const __bf16*)p.v_pages;
@@ -156,7 +168,7 @@ __global__ __launch_bounds__(NWU * 64, ATTN_DECODE_WAVES_PER_SIMD) void decode_s
     if (pg - tbase >= 64) {
       tbase = pg;
       const int mine = pg + lane;
-      tcache = mine < pg_end ? table[mine] : 0;
+      tcache = mine < np ? table[mine] : 0;
     }
     return __builtin_amdgcn_readlane(tcache, pg - tbase);
   };
@@ -176,12 +188,14 @@ __global__ __launch_bounds__(NWU * 64, ATTN_DECODE_WAVES_PER_SIMD) void decode_s
   // consume one page whose K and V are already in registers
   auto consume = [&](int pg, const u32x4_t (&kr)[C::KS], const u32x4_t (&vr)[C::VCH]) {
     const int valid = min(PAGE, L - pg * PAGE);  // slots of this page that hold tokens
-    // stage V (zeros in unused slots)
+    const int lo_slot = lo_t - pg * PAGE, sink_slot = p.n_sink - pg * PAGE;
+    auto visible = [&](int slot) { return slot < valid && (slot >= lo_slot || slot < sink_slot); };
+    // stage V (zeros in slots that are not visible)
 #pragma unroll
     for (int i = 0; i < C::VCH; ++i) {
       const int ch = lane + 64 * i;
       const int slot = ch / (D / 8), dch = ch - slot * (D / 8);
-      const u32x4_t val = slot < valid ? vr[i] : u32x4_t{0u, 0u, 0u, 0u};
+      const u32x4_t val = visible(slot) ? vr[i] : u32x4_t{0u, 0u, 0u, 0u};
       *(u32x4_t*)(vst + slot * C::VROW + dch * 16) = val;
     }
 
@@ -195,7 +209,7 @@ __global__ __launch_bounds__(NWU * 64, ATTN_DECODE_WAVES_PER_SIMD) void decode_s
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int slot = rg * 4 + e;
-      sv[e] = slot < valid ? sacc[e] * p.scale_log2 : kNegInf;
+      sv[e] = visible(slot) ? sacc[e] * p.scale_log2 : kNegInf;
       mx = fmaxf(mx, sv[e]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -230,32 +244,32 @@ __global__ __launch_bounds__(NWU * 64, ATTN_DECODE_WAVES_PER_SIMD) void decode_s
   // Walk the split's pages with ATTN_DECODE_PREFETCH pages of loads in
   // flight; the register buffers rotate by unrolling, so they are never
   // indexed at run time.
-  int pg = pg_begin;
+  int vi = v_begin;
 #if ATTN_DECODE_PREFETCH == 1
   u32x4_t ka[C::KS], va[C::VCH], kb[C::KS], vb[C::VCH];
-  if (pg < pg_end) load_page(pg, ka, va);
-  while (pg < pg_end) {
-    if (pg + 1 < pg_end) load_page(pg + 1, kb, vb);
-    consume(pg, ka, va);
-    if (++pg >= pg_end) break;
-    if (pg + 1 < pg_end) load_page(pg + 1, ka, va);
-    consume(pg, kb, vb);
-    ++pg;
+  if (vi < v_end) load_page(page_of(vi), ka, va);
+  while (vi < v_end) {
+    if (vi + 1 < v_end) load_page(page_of(vi + 1), kb, vb);
+    consume(page_of(vi), ka, va);
+    if (++vi >= v_end) break;
+    if (vi + 1 < v_end) load_page(page_of(vi + 1), ka, va);
+    consume(page_of(vi), kb, vb);
+    ++vi;
   }
 #else
   u32x4_t ka[C::KS], va[C::VCH], kb[C::KS], vb[C::VCH], kc[C::KS], vc[C::VCH];
-  if (pg < pg_end) load_page(pg, ka, va);
-  if (pg + 1 < pg_end) load_page(pg + 1, kb, vb);
-  while (pg < pg_end) {
-    if (pg + 2 < pg_end) load_page(pg + 2, kc, vc);
-    consume(pg, ka, va);
-    if (++pg >= pg_end) break;
-    if (pg + 2 < pg_end) load_page(pg + 2, ka, va);
-    consume(pg, kb, vb);
-    if (++pg >= pg_end) break;
-    if (pg + 2 < pg_end) load_page(pg + 2, kb, vb);
-    consume(pg, kc, vc);
-    ++pg;
+  if (vi < v_end) load_page(page_of(vi), ka, va);
+  if (vi + 1 < v_end) load_page(page_of(vi + 1), kb, vb);
+  while (vi < v_end) {
+    if (vi + 2 < v_end) load_page(page_of(vi + 2), kc, vc);
+    consume(page_of(vi), ka, va);
+    if (++vi >= v_end) break;
+    if (vi + 2 < v_end) load_page(page_of(vi + 2), ka, va);
+    consume(page_of(vi), kb, vb);
+    if (++vi >= v_end) break;
+    if (vi + 2 < v_end) load_page(page_of(vi + 2), kb, vb);
+    consume(page_of(vi), kc, vc);
+    ++vi;
   }
 #endif
 
@@ -296,13 +310,15 @@ __global__ __launch_bounds__(MERGE_THREADS) void decode_merge_kernel(DecodeParam
   const float* ml = p.ws_ml + (long long)bh * S * 2;
   const float* po = p.ws_o + (long long)bh * S * D;
 
+  // a learned sink logit is one more partial: m = s_h, l = 1, O = 0
+  const float sink = p.sinks ? p.sinks[bh % p.Hq] * 1.4426950408889634f : kNegInf;
   float M = kNegInf;
   for (int s = tid; s < S; s += MERGE_THREADS) M = fmaxf(M, ml[2 * s]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   if (lane == 0) red[wv] = M;
   __syncthreads();
-  M = red[0];
+  M = fmaxf(red[0], sink);
 #pragma unroll
   for (int i = 1; i < MERGE_THREADS / 64; ++i) M = fmaxf(M, red[i]);
   __syncthreads();
@@ -317,7 +333,7 @@ __global__ __launch_bounds__(MERGE_THREADS) void decode_merge_kernel(DecodeParam
   for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
   if (lane == 0) red[wv] = den;
   __syncthreads();
-  den = 0.f;
+  den = (p.sinks && M != kNegInf) ? __builtin_amdgcn_exp2f(sink - M) : 0.f;
 #pragma unroll
   for (int i = 0; i < MERGE_THREADS / 64; ++i) den += red[i];
 

@@ -241,13 +241,37 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+  // A learned sink logit s_h is an extra score column with zero value: it
+  // enters as the initial state m = s_h, l = e^0 = 1, O = 0.
   float m_ref = kNegInf, l_run = 0.f;
+  if (p.sinks) {
+    m_ref = p.sinks[h] * 1.4426950408889634f;  // base-2 units, like the scores
+    l_run = h2 == 0 ? 1.f : 0.f;  // the two lane halves' sums are added at the end
+  }
 
+  // ---- the key tiles this work-group visits -------------------------------------
+  // Tiles past the causal limit of the last row are never visited; with a
+  // window W, neither are the tiles before the window of the first row,
+  // except the tiles holding the n_sink initial positions. The visited tiles
+  // are numbered by "slots": sink tiles first, then the window tiles.
   const int q_last_wg = min(q_tile0 + C::BM, Nq) - 1;
   const int k_tiles = (Nk + BN - 1) / BN;
   const int n_tiles = p.causal ? min(k_tiles, (P + q_last_wg) / BN + 1) : k_tiles;
-  // tiles 0 .. wave_tiles-1 hold keys visible to some row of this wave
-  const int wave_tiles = (qw0 >= Nq) ? 0 : (p.causal ? min(n_tiles, (P + qw0 + 31) / BN + 1) : n_tiles);
+  const int W = p.window;
+  const int sink_tiles = (W > 0 && p.n_sink > 0) ? min((p.n_sink + BN - 1) / BN, n_tiles) : 0;
+  const int win_lo = W > 0 ? max(max(P + q_tile0 - W + 1, 0) / BN, sink_tiles) : 0;
+  const int n_slots = sink_tiles + max(n_tiles - win_lo, 0);
+  auto tile_of = [&](int j) { return j < sink_tiles ? j : win_lo + (j - sink_tiles); };
+  auto slot_of = [&](int t) { return t < sink_tiles ? t : t - win_lo + sink_tiles; };
+  // slots w_first .. w_end-1 hold keys visible to some row of this wave (with
+  // initial-token tiles, the slots between them and the wave's window are
+  // included and fully masked)
+  int w_first = 0, w_end = 0;
+  if (qw0 < Nq) {
+    const int last = (p.causal ? min(n_tiles, (P + qw0 + 31) / BN + 1) : n_tiles) - 1;
+    w_end = slot_of(last) + 1;
+    if (W > 0 && sink_tiles == 0) w_first = slot_of(max(P + qw0 - W + 1, 0) / BN);
+  }
 
   // ---- HBM -> LDS copies of K/V tiles ----------------------------------------------
   // Buffer i of the ring: K tile at lds + i*TILE, V tile VREG bytes further.
@@ -277,7 +301,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   const long long page_bytes = (long long)row_bytes * kPage;
   // issue the copies of tile t (this wave's share: instructions wave, wave+NW, ...)
   auto issue_tile = [&](int t, unsigned char* __restrict__ kl) {
-    const int k0 = t * BN;
+    const int k0 = tile_of(t) * BN;
     unsigned char* const vl = kl + C::VREG;
     const bool ragged = k0 + BN > Nk;
 #pragma unroll
@@ -380,17 +404,22 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   // mask tile t where it reaches past the diagonal or the end, then move the
   // reference max if this tile's max exceeds it by more than the threshold
   auto prep = [&](int t, f32x16_t (&s)[C::KB]) {
-    const int k0 = t * BN;
-    if ((p.causal && k0 + BN - 1 > P + qw0) || (k0 + BN > Nk)) {
+    const int k0 = tile_of(t) * BN;
+    const bool win_cut = W > 0 && k0 < P + qw0 + 31 - W + 1 && k0 + BN > p.n_sink;
+    if ((p.causal && k0 + BN - 1 > P + qw0) || (k0 + BN > Nk) || win_cut) {
       // key k0 + h2*4 + off (off a compile-time constant per element) is visible
-      // iff off <= lim
-      const int lim = (p.causal ? min(P + qi, Nk - 1) : Nk - 1) - k0 - h2 * 4;
+      // iff off <= lim, and with a window iff also off >= lo or it is one of
+      // the n_sink initial positions (off < sk)
+      const int base = k0 + h2 * 4;
+      const int lim = (p.causal ? min(P + qi, Nk - 1) : Nk - 1) - base;
+      const int lo = W > 0 ? P + qi - W + 1 - base : -BN;
+      const int sk = p.n_sink - base;
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int off = kb * 32 + (e >> 2) * 8 + (e & 3);
-          s[kb][e] = (off > lim) ? kNegInf : s[kb][e];
+          s[kb][e] = (off > lim || (off < lo && off >= sk)) ? kNegInf : s[kb][e];
         }
     }
     float mr = kNegInf;
@@ -449,31 +478,31 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
       }
   };
 
-  // ---- prologue: tiles 0, 1, 2 in flight; scores of tile 0 -------------------------
+  // ---- prologue: slots 0, 1, 2 in flight; scores of slot 0 -------------------------
   f32x16_t sa[C::KB], sb[C::KB];
-  issue_tile(0, kbuf(0));
-  if (n_tiles > 1) issue_tile(1, kbuf(1));
-  if (n_tiles > 2) {
+  if (n_slots > 0) issue_tile(0, kbuf(0));
+  if (n_slots > 1) issue_tile(1, kbuf(1));
+  if (n_slots > 2) {
     issue_tile(2, kbuf(2));
-    wait_vmcnt<kLoadsPerTile>();  // tiles 0 and 1 have landed
+    wait_vmcnt<kLoadsPerTile>();  // slots 0 and 1 have landed
   } else {
     wait_vmcnt<0>();
   }
   __syncthreads();
-  if (wave_tiles > 0) {
+  if (w_first == 0 && w_end > 0) {
     qk(kbuf(0), sa);
     prep(0, sa);
   }
 
-  // ---- main loop: iteration j consumes tile j and computes the scores of j+1 -------
-  // Every wave runs n_tiles iterations (one barrier each); the loops only
-  // differ in how much of the tile work the wave still has. Tile j+3 is
-  // issued at the top of iteration j into the buffer tile j-1 used; tile j+2
+  // ---- main loop: iteration j consumes slot j and computes the scores of j+1 -------
+  // Every wave runs n_slots iterations (one barrier each); the loops only
+  // differ in how much of the tile work the wave has in each. Slot j+3 is
+  // issued at the top of iteration j into the buffer slot j-1 used; slot j+2
   // must have landed before the barrier that ends iteration j. The buffers
   // reach the steps as distinct restrict pointers, which tells the compiler
-  // that reading tiles j and j+1 need not wait for the copy into j+3.
+  // that reading slots j and j+1 need not wait for the copy into j+3.
   auto end_iteration = [&](int j) {
-    if (j + 3 < n_tiles)
+    if (j + 3 < n_slots)
       wait_vmcnt<kLoadsPerTile>();
     else
       wait_vmcnt<0>();
@@ -484,19 +513,45 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
                        const unsigned char* __restrict__ b_v, const f32x16_t (&s_cur)[C::KB],
                        f32x16_t (&s_nxt)[C::KB]) {
     refresh_parts();
-    if (j + 3 < n_tiles) issue_tile(j + 3, b_issue);
+    if (j + 3 < n_slots) issue_tile(j + 3, b_issue);
     qk(b_k, s_nxt);  // scores of tile j+1, in flight while tile j is exponentiated
     pv(b_v, s_cur);
   };
   auto last_step = [&](int j, unsigned char* __restrict__ b_issue, const unsigned char* __restrict__ b_v) {
-    if (j + 3 < n_tiles) issue_tile(j + 3, b_issue);
+    if (j + 3 < n_slots) issue_tile(j + 3, b_issue);
     pv(b_v, sa);
   };
-  // Tiles j .. j+4 all have work for this wave: unrolled by four, so the
+  // the scores of slot j+1, the first of this wave's slots
+  auto first_step = [&](int j, unsigned char* __restrict__ b_issue, const unsigned char* __restrict__ b_k) {
+    refresh_parts();
+    if (j + 3 < n_slots) issue_tile(j + 3, b_issue);
+    qk(b_k, sa);
+  };
+  auto single_step = [&](int j) {  // a full step with run-time ring positions
+    full_step(j, kbuf(j + 3), kbuf(j + 1), vbuf(j), sa, sb);
+    prep(j + 1, sb);
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) sa[kb] = sb[kb];
+    end_iteration(j);
+  };
+  auto idle_step = [&](int j) {  // no work for this wave: keep loading slots for the others
+    if (j + 3 < n_slots) issue_tile(j + 3, kbuf(j + 3));
+    end_iteration(j);
+  };
+  int j = 0;
+  for (; j + 1 < w_first; ++j) idle_step(j);
+  if (w_first > 0 && w_first < w_end) {
+    first_step(j, kbuf(j + 3), kbuf(j + 1));
+    prep(j + 1, sa);
+    end_iteration(j);
+    ++j;
+  }
+  // (from here j == w_first) up to the next multiple of four one step at a time
+  for (; (j & 3) && j + 1 < w_end; ++j) single_step(j);
+  // Slots j .. j+4 all have work for this wave: unrolled by four, so the
   // ring positions are compile-time constants (j is a multiple of four) and
   // the score registers alternate instead of being copied.
-  int j = 0;
-  for (; j + 4 < wave_tiles; j += 4) {
+  for (; j + 4 < w_end; j += 4) {
     full_step(j, kbuf(3), kbuf(1), vbuf(0), sa, sb);
     prep(j + 1, sb);
     end_iteration(j);
@@ -510,22 +565,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
     prep(j + 4, sa);
     end_iteration(j + 3);
   }
-  for (; j + 1 < wave_tiles; ++j) {
-    full_step(j, kbuf(j + 3), kbuf(j + 1), vbuf(j), sa, sb);
-    prep(j + 1, sb);
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) sa[kb] = sb[kb];
-    end_iteration(j);
-  }
-  if (j < wave_tiles) {  // the wave's last tile
+  for (; j + 1 < w_end; ++j) single_step(j);
+  if (j < w_end) {  // the wave's last slot
     last_step(j, kbuf(j + 3), vbuf(j));
     end_iteration(j);
     ++j;
   }
-  for (; j < n_tiles; ++j) {  // no work left for this wave: keep loading tiles for the others
-    if (j + 3 < n_tiles) issue_tile(j + 3, kbuf(j + 3));
-    end_iteration(j);
-  }
+  for (; j < n_slots; ++j) idle_step(j);
 
   // ---- epilogue: O / l -> bf16, written as whole rows through LDS ---------------------
   // (every wave has passed the last barrier with no copy in flight, so the tile

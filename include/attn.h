@@ -87,6 +87,30 @@ enum { ATTN_F32 = 0, ATTN_BF16 = 1 };
 enum { ATTN_BNHD = 0, ATTN_BHND = 1 };
 
 /*
+ * attn_variant - optional changes to the causal mask and the softmax, shared
+ * by attn_prefill_ex, attn_prefill_paged and attn_decode_ex (NULL = none).
+ *
+ * window: 0, or W > 0: a key is visible to a query only if 0 <= p_q - p_k < W
+ *         (the window includes the query's own position) [SDPA] sections 4
+ *         and 9. Tiles outside every row's window are not visited.
+ * n_sink: 0, or S > 0 together with a window: the keys at positions 0..S-1
+ *         stay visible to every later query (StreamingLLM's initial-token
+ *         anchors, [SDPA] section 10).
+ * sinks:  NULL, or a device fp32 [Hq] array: a learned logit s_h per query
+ *         head, an extra score column that takes part in the softmax and
+ *         contributes no value ([SDPA] section 10):
+ *           o = sum_j e^(s_j - m) v_j / (sum_j e^(s_j - m) + e^(s_h - m)),
+ *         with m the row max over the visible scores and s_h. The lse output
+ *         includes the e^(s_h) term.
+ * The window and the initial-token anchors need causal attention.
+ */
+typedef struct attn_variant {
+  int window;
+  int n_sink;
+  const float* sinks;
+} attn_variant;
+
+/*
  * attn_prefill - causal GQA attention over whole sequences, bf16, [B, N, H, d].
  *
  * q: [B, N, Hq, d] bf16;  k, v: [B, N, Hkv, d] bf16;  o: [B, N, Hq, d] bf16 (out).
@@ -112,10 +136,12 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o,
  * lse:    NULL, or fp32 [B, Hq, N] (out): the natural logarithm of each row's
  *         softmax denominator, max_j s_ij + ln(sum_j e^(s_ij - max)), where
  *         s_ij = scale * q_i . k_j over the visible keys.
+ * variant: NULL, or window / initial tokens / sink logits (attn_variant);
+ *         any variant needs dtype ATTN_BF16, and a window needs causal != 0.
  */
 int attn_prefill_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                     int B, int N, int Hq, int Hkv, int d, float scale, int causal,
-                    int dtype, int layout, void* stream);
+                    int dtype, int layout, const attn_variant* variant, void* stream);
 
 /*
  * attn_decode_num_splits - the number of context splits attn_decode uses.
@@ -225,6 +251,8 @@ int attn_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_
  *              of each row, as for attn_prefill_ex.
  * total_q:     T, the rows of q and o (host); it fixes the lse layout.
  * max_q_len:   an upper bound on every c_b (host); it sizes the launch.
+ * variant:     NULL, or window / initial tokens / sink logits (attn_variant),
+ *              with positions counted from the start of the sequence.
  * Row i of sequence b, query head h, sees the keys at positions 0 .. P_b + i
  * (causality compares token positions [SDPA] section 4; after a prefix of P
  * tokens row i is at position P + i):
@@ -241,7 +269,21 @@ int attn_prefill_paged(const void* q, const void* k_pages, const void* v_pages,
                        const int32_t* block_table, const int32_t* cu_q, const int32_t* seq_lens,
                        void* o, float* lse, int B, int Hq, int Hkv, int d, int page_size,
                        int max_pages_per_seq, int num_pages, int total_q, int max_q_len,
-                       float scale, void* stream);
+                       float scale, const attn_variant* variant, void* stream);
+
+/*
+ * attn_decode_ex - attn_decode with a variant (NULL = none, the same as
+ * attn_decode): with a window W the query at position L-1 sees the tokens
+ * t >= L - W and t < n_sink, and only the pages holding them are read (the
+ * splits cut those pages); a sink logit joins the merge as one more partial
+ * with max s_h, sum 1 and zero output [SDPA] section 10. The workspace size
+ * and split count are those of attn_decode for the same arguments.
+ */
+int attn_decode_ex(const void* q, const void* k_pages, const void* v_pages,
+                   const int32_t* block_table, const int32_t* seq_lens, void* o,
+                   int B, int Hq, int Hkv, int d, int page_size, int max_pages_per_seq,
+                   int num_pages, float scale, int num_splits, const attn_variant* variant,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * attn_gather_pages - materialise the logical cache of each sequence from the

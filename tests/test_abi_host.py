@@ -32,7 +32,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     for n in names:
         assert hasattr(L, n), n
     assert sorted(n for n, _, _ in binding.SIGNATURES) == names
@@ -57,10 +57,14 @@ ERR = {n: header_enum(n) for n in ("ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_
 
 def prefill(L, **kw):
     a = dict(q=A, k=A, v=A, o=A, lse=None, B=1, N=8, Hq=4, Hkv=2, d=64, scale=0.125, causal=1,
-             dtype=1, layout=0)
+             dtype=1, layout=0, var=None)
     a.update(kw)
     return L.attn_prefill_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["N"], a["Hq"], a["Hkv"],
-                             a["d"], a["scale"], a["causal"], a["dtype"], a["layout"], None)
+                             a["d"], a["scale"], a["causal"], a["dtype"], a["layout"], a["var"], None)
+
+
+def var(window=0, n_sink=0, sinks=None):
+    return ctypes.pointer(binding.AttnVariant(window, n_sink, sinks))
 
 
 @pytest.mark.parametrize("kw,err", [
@@ -71,6 +75,9 @@ def prefill(L, **kw):
     (dict(scale=float("nan")), "ATTN_ERR_SHAPE"), (dict(scale=float("inf")), "ATTN_ERR_SHAPE"),
     (dict(q=A + 2), "ATTN_ERR_ALIGN"), (dict(v=A + 8), "ATTN_ERR_ALIGN"), (dict(lse=A + 1), "ATTN_ERR_ALIGN"),
     (dict(B=1 << 20, N=1 << 20, Hq=64, Hkv=8), "ATTN_ERR_SHAPE"),
+    (dict(var=var(window=-1)), "ATTN_ERR_SHAPE"), (dict(var=var(n_sink=4)), "ATTN_ERR_SHAPE"),
+    (dict(var=var(window=8), causal=0), "ATTN_ERR_SHAPE"), (dict(var=var(window=8), dtype=0), "ATTN_ERR_DTYPE"),
+    (dict(var=var(sinks=A + 2)), "ATTN_ERR_ALIGN"),
 ])
 def test_prefill_rejects(L, kw, err):
     assert prefill(L, **kw) == ERR[err]
@@ -83,11 +90,13 @@ def test_prefill_plain_entry_validates(L):
 
 def decode(L, **kw):
     a = dict(q=A, k=A, v=A, table=A, lens=A, o=A, B=2, Hq=8, Hkv=2, d=128, page_size=16, mpps=4,
-             num_pages=8, scale=0.1, splits=0, ws=A, ws_bytes=1 << 30)
+             num_pages=8, scale=0.1, splits=0, ws=A, ws_bytes=1 << 30, var=None)
     a.update(kw)
-    return L.attn_decode(a["q"], a["k"], a["v"], a["table"], a["lens"], a["o"], a["B"], a["Hq"], a["Hkv"],
-                         a["d"], a["page_size"], a["mpps"], a["num_pages"], a["scale"], a["splits"],
-                         a["ws"], a["ws_bytes"], None)
+    args = (a["q"], a["k"], a["v"], a["table"], a["lens"], a["o"], a["B"], a["Hq"], a["Hkv"],
+            a["d"], a["page_size"], a["mpps"], a["num_pages"], a["scale"], a["splits"])
+    if a["var"] is None:
+        return L.attn_decode(*args, a["ws"], a["ws_bytes"], None)
+    return L.attn_decode_ex(*args, a["var"], a["ws"], a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,err", [
@@ -98,6 +107,9 @@ def decode(L, **kw):
     (dict(ws=None), "ATTN_ERR_WORKSPACE"), (dict(ws_bytes=16), "ATTN_ERR_WORKSPACE"),
     (dict(k=A + 4), "ATTN_ERR_ALIGN"), (dict(table=A + 2), "ATTN_ERR_ALIGN"),
     (dict(mpps=1 << 28), "ATTN_ERR_SHAPE"),
+    (dict(var=var(window=-3)), "ATTN_ERR_SHAPE"), (dict(var=var(n_sink=2)), "ATTN_ERR_SHAPE"),
+    (dict(var=var(window=5, n_sink=-1)), "ATTN_ERR_SHAPE"), (dict(var=var(sinks=A + 1)), "ATTN_ERR_ALIGN"),
+    (dict(q=None, var=var(window=5)), "ATTN_ERR_NULL"),
 ])
 def test_decode_rejects(L, kw, err):
     assert decode(L, **kw) == ERR[err]
@@ -157,7 +169,7 @@ def paged(L, **kw):
     a.update(kw)
     return L.attn_prefill_paged(a["q"], a["kp"], a["vp"], a["table"], a["cu"], a["lens"], a["o"], a["lse"],
                                 a["B"], a["Hq"], a["Hkv"], a["d"], a["page_size"], a["mpps"],
-                                a["num_pages"], a["total"], a["max_q"], a["scale"], None)
+                                a["num_pages"], a["total"], a["max_q"], a["scale"], a.get("var"), None)
 
 
 @pytest.mark.parametrize("kw,err", [
@@ -166,6 +178,7 @@ def paged(L, **kw):
     (dict(Hq=6, Hkv=4), "ATTN_ERR_GQA"), (dict(d=32), "ATTN_ERR_HEAD_DIM"), (dict(page_size=8), "ATTN_ERR_PAGE"),
     (dict(scale=float("inf")), "ATTN_ERR_SHAPE"), (dict(o=A + 4), "ATTN_ERR_ALIGN"),
     (dict(lse=A + 2), "ATTN_ERR_ALIGN"), (dict(lens=A + 1), "ATTN_ERR_ALIGN"),
+    (dict(var=var(n_sink=1)), "ATTN_ERR_SHAPE"), (dict(var=var(window=-2)), "ATTN_ERR_SHAPE"),
 ])
 def test_prefill_paged_rejects(L, kw, err):
     assert paged(L, **kw) == ERR[err]

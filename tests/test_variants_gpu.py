@@ -1,0 +1,170 @@
+"""Sliding window, initial-token anchors and learned sink logits on the GPU
+(prefill, paged prefill and decode through the C ABI) against the CPU
+float64 oracle.
+
+Also checked: a window at least as long as the sequence is bit-identical to
+plain causal attention (the same tiles are visited in the same order), and
+key/value rows that lie outside every window of a chunk are never read
+(they hold NaN, which would reach the output through a zero weight).
+
+Tolerances against the fp64 oracle: bf16 inputs, fp32 accumulation,
+max-abs <= 2e-2 and mean-abs <= 5e-3; lse max-abs <= 1e-2.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_flashattention_amd import binding as bd
+from exact_attention_flashattention_amd import workloads as wl
+from oracle import attention_oracle as ao
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX, BF16_MEAN = 2e-2, 5e-3
+LSE_BF16 = 1e-2
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def bits(t):
+    return t.view(torch.int16)
+
+
+def sink_logits(Hq, seed):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.rand(Hq, generator=g) * 6.0 - 1.0).float()   # U[-1, 5): small to dominant
+
+
+def check(got, ref, lse=None, ref_lse=None):
+    e = np.abs(got.double().numpy() - ref)
+    log(f"  max-abs {e.max():.3e} mean-abs {e.mean():.3e}")
+    assert e.max() <= BF16_MAX and e.mean() <= BF16_MEAN
+    if lse is not None:
+        assert np.abs(lse.double().numpy() - ref_lse).max() <= LSE_BF16
+
+
+PREFILL_CASES = [
+    # B, N, Hq, Hkv, d, window, n_sink, sinks
+    (2, 300, 4, 2, 128, 1, 0, False),       # each row sees only itself
+    (1, 700, 8, 2, 128, 100, 0, False),     # window inside one tile width
+    (2, 520, 4, 4, 64, 33, 0, True),        # 32-key tiles, sinks too
+    (1, 900, 8, 1, 128, 257, 4, False),     # initial tokens + window, MQA
+    (1, 640, 4, 2, 128, 64, 70, True),      # anchors span two tiles
+    (2, 333, 4, 2, 128, 0, 0, True),        # sinks alone
+    (1, 1100, 8, 8, 64, 500, 1, True),      # several query tiles, everything on
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[f"case{i}" for i in range(len(PREFILL_CASES))])
+def test_prefill_variants(case):
+    B, N, Hq, Hkv, d, W, S, use_sinks = case
+    x = wl.prefill_inputs(B, N, Hq, Hkv, d, seed=700 + N)
+    sinks = sink_logits(Hq, 701) if use_sinks else None
+    log(f"case: B={B} N={N} Hq={Hq} Hkv={Hkv} d={d} window={W} n_sink={S} sinks={use_sinks}")
+    l = torch.full((B, Hq, N), float("nan"), device="cuda")
+    o = bd.attn_prefill_ex(x.q.cuda(), x.k.cuda(), x.v.cuda(), scale=x.scale, lse=l, window=W, n_sink=S,
+                           sinks=sinks.cuda() if use_sinks else None)
+    torch.cuda.synchronize()
+    ref, ref_lse = ao.prefill_variant_ref(x.q, x.k, x.v, x.scale, "BNHD", window=W or None, n_sink=S,
+                                          sinks=sinks.numpy() if use_sinks else None)
+    check(o.cpu(), ref, l.cpu(), ref_lse)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_window_covering_everything_is_plain_causal_bit_exact(d):
+    x = wl.prefill_inputs(2, 450, 8, 2, d, seed=720 + d)
+    q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+    plain = bd.attn_prefill_ex(q, k, v, scale=x.scale)
+    wide = bd.attn_prefill_ex(q, k, v, scale=x.scale, window=450)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(plain.cpu()), bits(wide.cpu()))
+
+
+PAGED_CASES = [
+    # B, Hq, Hkv, d, prefix, chunk, window, n_sink, sinks
+    (3, 8, 2, 128, [0, 300, 2000], [64, 100, 300], 256, 0, False),
+    (2, 4, 4, 64, [17, 1000], [33, 129], 77, 3, True),
+    (2, 8, 1, 128, [5000, 40], [513, 7], 1024, 16, True),
+]
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=[f"case{i}" for i in range(len(PAGED_CASES))])
+def test_paged_prefill_variants(case):
+    B, Hq, Hkv, d, P, c, W, S, use_sinks = case
+    x = wl.chunked_prefill_inputs(B, Hq, Hkv, d, P, c, seed=740 + sum(c))
+    wl.poison_chunk_slots(x)
+    sinks = sink_logits(Hq, 741) if use_sinks else None
+    log(f"case: B={B} Hq={Hq} Hkv={Hkv} d={d} prefix={P} chunk={c} window={W} n_sink={S} sinks={use_sinks}")
+    ref_kp, ref_vp = ao.kv_append_ref(x.k_pages, x.v_pages, x.block_table, x.k_new, x.v_new,
+                                      x.cu_q, x.prefix_lens)
+    # rows no chunk row can see (before every window, past the anchors, away
+    # from the first visited tile) become NaN in the pools the GPU gets
+    kp_g, vp_g = ref_kp.clone(), ref_vp.clone()
+    poisoned = 0
+    for b in range(B):
+        first_visible = P[b] - W + 1
+        cut = (first_visible // 128) * 128 - 128
+        start = 128 if S else 0  # keep the anchor tiles whole
+        for t in range(start, max(cut, start)):
+            page = int(x.block_table[b, t // 16])
+            kp_g[page, t % 16] = float("nan")
+            vp_g[page, t % 16] = float("nan")
+            poisoned += 1
+    log(f"  poisoned rows: {poisoned}")
+    l = torch.full((Hq, x.total_q), float("nan"), device="cuda")
+    o = bd.attn_prefill_paged(x.q.cuda(), kp_g.cuda(), vp_g.cuda(), x.block_table.cuda(), x.cu_q.cuda(),
+                              x.seq_lens.cuda(), scale=x.scale, lse=l, window=W, n_sink=S,
+                              sinks=sinks.cuda() if use_sinks else None)
+    torch.cuda.synchronize()
+    ref, ref_lse = ao.paged_prefill_ref(x.q, ref_kp, ref_vp, x.block_table, x.cu_q, x.seq_lens, x.scale,
+                                        window=W, n_sink=S, sinks=sinks.numpy() if use_sinks else None)
+    check(o.cpu(), ref, l.cpu(), ref_lse)
+
+
+DECODE_CASES = [
+    # B, Hq, Hkv, d, seq_lens, window, n_sink, sinks, splits
+    (4, 8, 2, 128, [1, 17, 300, 1000], 16, 0, False, 0),
+    (3, 16, 2, 64, [50, 513, 2000], 100, 4, True, 0),
+    (2, 8, 8, 128, [4096, 3000], 1000, 0, True, 7),
+    (2, 32, 1, 128, [700, 33], 0, 0, True, 3),          # sinks alone
+    (3, 8, 2, 128, [0, 5, 64], 8, 2, True, 0),          # an empty sequence
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[f"case{i}" for i in range(len(DECODE_CASES))])
+def test_decode_variants(case):
+    B, Hq, Hkv, d, lens, W, S, use_sinks, splits = case
+    x = wl.paged_decode_inputs(B, Hq, Hkv, d, lens, seed=760 + sum(lens))
+    wl.poison_unused_slots(x)
+    sinks = sink_logits(Hq, 761) if use_sinks else None
+    log(f"case: B={B} Hq={Hq} Hkv={Hkv} d={d} lens={lens} window={W} n_sink={S} sinks={use_sinks} splits={splits}")
+    o = bd.attn_decode_ex(x.q.cuda(), x.k_pages.cuda(), x.v_pages.cuda(), x.block_table.cuda(),
+                          x.seq_lens.cuda(), scale=x.scale, num_splits=splits, window=W, n_sink=S,
+                          sinks=sinks.cuda() if use_sinks else None)
+    torch.cuda.synchronize()
+    ref = ao.decode_ref(x.q, x.k_pages, x.v_pages, x.block_table, x.seq_lens, x.scale,
+                        window=W or None, n_sink=S, sinks=sinks.numpy() if use_sinks else None)
+    check(o.cpu(), ref)
+
+
+def test_decode_variant_is_the_last_prefill_row():
+    B, N, Hq, Hkv, d, W, S = 2, 608, 8, 2, 128, 200, 5
+    x = wl.prefill_inputs(B, N, Hq, Hkv, d, seed=780)
+    sinks = sink_logits(Hq, 781).cuda()
+    pre = bd.attn_prefill_ex(x.q.cuda(), x.k.cuda(), x.v.cuda(), scale=x.scale, window=W, n_sink=S, sinks=sinks)
+    pages = B * N // 16  # identity table: sequence b's tokens fill pages b*N/16 ..
+    kp = x.k.reshape(pages, 16, Hkv, d).contiguous().cuda()
+    vp = x.v.reshape(pages, 16, Hkv, d).contiguous().cuda()
+    table = torch.arange(pages, dtype=torch.int32).reshape(B, -1).cuda()
+    lens = torch.tensor([N] * B, dtype=torch.int32).cuda()
+    dec = bd.attn_decode_ex(x.q[:, N - 1].contiguous().cuda(), kp, vp, table, lens, scale=x.scale,
+                            window=W, n_sink=S, sinks=sinks)
+    torch.cuda.synchronize()
+    e = (dec.cpu().double() - pre[:, N - 1].cpu().double()).abs().max().item()
+    log(f"  decode vs prefill last row: {e:.3e}")
+    assert e <= 2 * BF16_MAX
