@@ -261,8 +261,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   const int sink_tiles = (W > 0 && p.n_sink > 0) ? min((p.n_sink + BN - 1) / BN, n_tiles) : 0;
   const int win_lo = W > 0 ? max(max(P + q_tile0 - W + 1, 0) / BN, sink_tiles) : 0;
   const int n_slots = sink_tiles + max(n_tiles - win_lo, 0);
-  auto tile_of = [&](int j) { return j < sink_tiles ? j : win_lo + (j - sink_tiles); };
-  auto slot_of = [&](int t) { return t < sink_tiles ? t : t - win_lo + sink_tiles; };
+  auto tile_of = [&](int j) __attribute__((always_inline)) { return j < sink_tiles ? j : win_lo + (j - sink_tiles); };
+  auto slot_of = [&](int t) __attribute__((always_inline)) { return t < sink_tiles ? t : t - win_lo + sink_tiles; };
   // slots w_first .. w_end-1 hold keys visible to some row of this wave (with
   // initial-token tiles, the slots between them and the wave's window are
   // included and fully masked)
@@ -278,8 +278,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   // With the K and V tiles in separate halves every LDS read below is a
   // per-lane register plus an immediate offset below 64 KiB, so once the ring
   // position is a compile-time constant no address arithmetic is left.
-  auto kbuf = [&](int t) { return lds + (t % C::NBUF) * C::TILE; };
-  auto vbuf = [&](int t) { return lds + C::VREG + (t % C::NBUF) * C::TILE; };
+  auto kbuf = [&](int t) __attribute__((always_inline)) { return lds + (t % C::NBUF) * C::TILE; };
+  auto vbuf = [&](int t) __attribute__((always_inline)) { return lds + C::VREG + (t % C::NBUF) * C::TILE; };
   // This lane's part of a load instruction: tile-local row, logical chunk and
   // the byte offset from the tile's first row (rows are k_sn elements apart).
   const int ld_row = lane / C::CPR;
@@ -300,7 +300,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
             : nullptr;
   const long long page_bytes = (long long)row_bytes * kPage;
   // issue the copies of tile t (this wave's share: instructions wave, wave+NW, ...)
-  auto issue_tile = [&](int t, unsigned char* __restrict__ kl) {
+  auto issue_tile = [&](int t, unsigned char* __restrict__ kl) __attribute__((always_inline)) {
     const int k0 = tile_of(t) * BN;
     unsigned char* const vl = kl + C::VREG;
     const bool ragged = k0 + BN > Nk;
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   // Hide the lane parts from loop-invariant code motion once per tile step:
   // otherwise every (buffer, read) address of the unrolled loop is hoisted
   // into a register of its own, far more than the register file holds.
-  auto refresh_parts = [&]() {
+  auto refresh_parts = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int s_ = 0; s_ < C::KS; ++s_) asm volatile("" : "+v"(kpart[s_]));
 #pragma unroll
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
 
   // ---- the three steps of a tile ----------------------------------------------
   // S^T = K Q^T for tile t
-  auto qk = [&](const unsigned char* __restrict__ k_lds, f32x16_t (&s)[C::KB]) {
+  auto qk = [&](const unsigned char* __restrict__ k_lds, f32x16_t (&s)[C::KB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
@@ -403,7 +403,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   };
   // mask tile t where it reaches past the diagonal or the end, then move the
   // reference max if this tile's max exceeds it by more than the threshold
-  auto prep = [&](int t, f32x16_t (&s)[C::KB]) {
+  auto prep = [&](int t, f32x16_t (&s)[C::KB]) __attribute__((always_inline)) {
     const int k0 = tile_of(t) * BN;
     const bool win_cut = W > 0 && k0 < P + qw0 + 31 - W + 1 && k0 + BN > p.n_sink;
     if ((p.causal && k0 + BN - 1 > P + qw0) || (k0 + BN > Nk) || win_cut) {
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
     }
   };
   // P = 2^(s - m) rounded to bf16, l += rowsum(P), O^T += V^T P^T for tile t
-  auto pv = [&](const unsigned char* __restrict__ vt_lds, const f32x16_t (&s)[C::KB]) {  // V tile of tile j
+  auto pv = [&](const unsigned char* __restrict__ vt_lds, const f32x16_t (&s)[C::KB]) __attribute__((always_inline)) {  // V tile of tile j
     const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
     u32x4_t pop[C::PS];
     float rs0 = 0.f, rs1 = 0.f;
@@ -489,10 +489,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
     wait_vmcnt<0>();
   }
   __syncthreads();
-  if (w_first == 0 && w_end > 0) {
-    qk(kbuf(0), sa);
-    prep(0, sa);
-  }
+  if (w_first == 0 && w_end > 0) qk(kbuf(0), sa);
 
   // ---- main loop: iteration j consumes slot j and computes the scores of j+1 -------
   // Every wave runs n_slots iterations (one barrier each); the loops only
@@ -501,40 +498,44 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   // must have landed before the barrier that ends iteration j. The buffers
   // reach the steps as distinct restrict pointers, which tells the compiler
   // that reading slots j and j+1 need not wait for the copy into j+3.
-  auto end_iteration = [&](int j) {
+  auto end_iteration = [&](int j) __attribute__((always_inline)) {
     if (j + 3 < n_slots)
       wait_vmcnt<kLoadsPerTile>();
     else
       wait_vmcnt<0>();
     __syncthreads();
   };
-  // b_issue: buffer receiving tile j+3; b_k: K tile of tile j+1; b_v: V tile of tile j
+  // b_issue: buffer receiving tile j+3; b_k: K tile of tile j+1; b_v: V tile of tile j.
+  // The scores of tile j were computed in the previous iteration, so their
+  // row max (prep) does not wait on an MFMA result and fills the shadow of
+  // the MFMAs of tile j+1's scores; exponentiation then overlaps P V.
   auto full_step = [&](int j, unsigned char* __restrict__ b_issue, const unsigned char* __restrict__ b_k,
-                       const unsigned char* __restrict__ b_v, const f32x16_t (&s_cur)[C::KB],
-                       f32x16_t (&s_nxt)[C::KB]) {
+                       const unsigned char* __restrict__ b_v, f32x16_t (&s_cur)[C::KB],
+                       f32x16_t (&s_nxt)[C::KB]) __attribute__((always_inline)) {
     refresh_parts();
     if (j + 3 < n_slots) issue_tile(j + 3, b_issue);
-    qk(b_k, s_nxt);  // scores of tile j+1, in flight while tile j is exponentiated
+    qk(b_k, s_nxt);  // scores of tile j+1
+    prep(j, s_cur);
     pv(b_v, s_cur);
   };
-  auto last_step = [&](int j, unsigned char* __restrict__ b_issue, const unsigned char* __restrict__ b_v) {
+  auto last_step = [&](int j, unsigned char* __restrict__ b_issue, const unsigned char* __restrict__ b_v) __attribute__((always_inline)) {
     if (j + 3 < n_slots) issue_tile(j + 3, b_issue);
+    prep(j, sa);
     pv(b_v, sa);
   };
   // the scores of slot j+1, the first of this wave's slots
-  auto first_step = [&](int j, unsigned char* __restrict__ b_issue, const unsigned char* __restrict__ b_k) {
+  auto first_step = [&](int j, unsigned char* __restrict__ b_issue, const unsigned char* __restrict__ b_k) __attribute__((always_inline)) {
     refresh_parts();
     if (j + 3 < n_slots) issue_tile(j + 3, b_issue);
     qk(b_k, sa);
   };
-  auto single_step = [&](int j) {  // a full step with run-time ring positions
+  auto single_step = [&](int j) __attribute__((always_inline)) {  // a full step with run-time ring positions
     full_step(j, kbuf(j + 3), kbuf(j + 1), vbuf(j), sa, sb);
-    prep(j + 1, sb);
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) sa[kb] = sb[kb];
     end_iteration(j);
   };
-  auto idle_step = [&](int j) {  // no work for this wave: keep loading slots for the others
+  auto idle_step = [&](int j) __attribute__((always_inline)) {  // no work for this wave: keep loading slots for the others
     if (j + 3 < n_slots) issue_tile(j + 3, kbuf(j + 3));
     end_iteration(j);
   };
@@ -542,7 +543,6 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   for (; j + 1 < w_first; ++j) idle_step(j);
   if (w_first > 0 && w_first < w_end) {
     first_step(j, kbuf(j + 3), kbuf(j + 1));
-    prep(j + 1, sa);
     end_iteration(j);
     ++j;
   }
@@ -553,16 +553,12 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   // the score registers alternate instead of being copied.
   for (; j + 4 < w_end; j += 4) {
     full_step(j, kbuf(3), kbuf(1), vbuf(0), sa, sb);
-    prep(j + 1, sb);
     end_iteration(j);
     full_step(j + 1, kbuf(0), kbuf(2), vbuf(1), sb, sa);
-    prep(j + 2, sa);
     end_iteration(j + 1);
     full_step(j + 2, kbuf(1), kbuf(3), vbuf(2), sa, sb);
-    prep(j + 3, sb);
     end_iteration(j + 2);
     full_step(j + 3, kbuf(2), kbuf(0), vbuf(3), sb, sa);
-    prep(j + 4, sa);
     end_iteration(j + 3);
   }
   for (; j + 1 < w_end; ++j) single_step(j);
