@@ -176,11 +176,13 @@ def chunked_report(dev, stream, steps: int) -> dict:
                           "flops_per_launch": fl,
                           "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS,
                                        "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                                       "traffic": measured_traffic("prefill_paged", PREFILL_SOURCES),
                                        "kernel": "prefill_bf16_kernel<128,8,64,paged>"}},
         "kv_append": {"value": round(gb, 2), "unit": "GB/s", "avg_launch_us": round(t_app, 2),
                       "bytes_per_launch": by,
                       "roofline": {"bound": "hbm", "achieved": round(gb, 2), "peak": HBM_PEAK_GBS,
                                    "unit": "GB/s", "frac": round(gb / HBM_PEAK_GBS, 4),
+                                   "traffic": measured_traffic("kv_append", APPEND_SOURCES),
                                    "kernel": "kv_append_kernel"}},
     }
 
@@ -243,13 +245,15 @@ def variants_report(dev, stream, steps: int) -> dict:
 
 PREFILL_SOURCES = ["prefill_bf16.hip", "attn_internal.h"]
 DECODE_SOURCES = ["decode.hip", "attn_internal.h"]
+APPEND_SOURCES = ["kv_append.hip", "attn_internal.h"]
 
 
 def write_traffic(root: str) -> int:
     """Turn rocprofv3 --pmc CSVs into profiles/traffic.json (no GPU needed).
 
     Expects <root>/<COUNTER>_<kind>/**/*counter_collection.csv for COUNTER in
-    FETCH_SIZE, WRITE_SIZE and kind in prefill, decode, copy, as written by
+    FETCH_SIZE, WRITE_SIZE and kind in prefill, decode, chunked, append, copy,
+    as written by
         rocprofv3 --pmc <COUNTER> -d <root>/<COUNTER>_<kind> -o run --output-format csv \
             -- python bench.py --only <kind> --steps 3 --warmup 1 > <root>/<COUNTER>_<kind>.log
     Each counter (KiB per dispatch) is scaled by the ratio between the bytes a
@@ -277,7 +281,9 @@ def write_traffic(root: str) -> int:
                            "write_factor": round(write_factor, 4)}}
     for key, kind, parts, srcs in [("prefill_bf16", "prefill", ["prefill_bf16_kernel"], PREFILL_SOURCES),
                                    ("decode", "decode", ["decode_split_kernel", "decode_merge_kernel"],
-                                    DECODE_SOURCES)]:
+                                    DECODE_SOURCES),
+                                   ("prefill_paged", "chunked", ["prefill_bf16_kernel"], PREFILL_SOURCES),
+                                   ("kv_append", "append", ["kv_append_kernel"], APPEND_SOURCES)]:
         for counter in ("FETCH_SIZE", "WRITE_SIZE"):
             ran = None
             with open(os.path.join(root, f"{counter}_{kind}.log")) as f:
@@ -338,7 +344,7 @@ def only(args, dev) -> int:
     b.record(stream)
     torch.cuda.synchronize()
     srcs = {"prefill": PREFILL_SOURCES, "decode": DECODE_SOURCES, "chunked": PREFILL_SOURCES,
-            "append": ["kv_append.hip"]}.get(args.only)
+            "append": APPEND_SOURCES}.get(args.only)
     print(json.dumps({"only": args.only, "steps": args.steps,
                       "avg_us": round(a.elapsed_time(b) * 1e3 / args.steps, 2),
                       "source_sha256": source_hash(*srcs) if srcs else None, **work}), flush=True)
