@@ -278,6 +278,50 @@ def test_decode_ragged_lengths_and_empty_sequence():
         assert np.abs(dec[b] - ref).max() <= 1e-12
 
 
+# ------------------------------------------------------------ backward
+
+@pytest.mark.parametrize("Hq,Hkv,causal", [(4, 2, True), (4, 4, False), (6, 1, True)])
+def test_backward_matches_torch_autograd_fp64(Hq, Hkv, causal):
+    B, N, d, scale = 2, 13, 8, 0.4
+    q, k, v, do = rnd((B, Hq, N, d), 180), rnd((B, Hkv, N, d), 181), rnd((B, Hkv, N, d), 182), rnd((B, Hq, N, d), 183)
+    dq, dk, dv = ao.sdpa_backward_ref(q, k, v, do, scale, causal)
+    tq, tk, tv = (torch.from_numpy(a).requires_grad_() for a in (q, k, v))
+    o = F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale, enable_gqa=True)
+    o.backward(torch.from_numpy(do))
+    assert np.abs(dq - tq.grad.numpy()).max() <= 1e-12
+    assert np.abs(dk - tk.grad.numpy()).max() <= 1e-12
+    assert np.abs(dv - tv.grad.numpy()).max() <= 1e-12
+
+
+def test_backward_matches_central_differences_of_the_forward():
+    B, Hq, Hkv, N, d, scale = 1, 2, 1, 5, 3, 0.7
+    q, k, v, do = rnd((B, Hq, N, d), 190), rnd((B, Hkv, N, d), 191), rnd((B, Hkv, N, d), 192), rnd((B, Hq, N, d), 193)
+    dq, dk, dv = ao.sdpa_backward_ref(q, k, v, do, scale, True)
+
+    def loss(qq, kk, vv):
+        o, _ = ao.sdpa_ref(qq, kk, vv, scale, causal=True)
+        return float((o * do).sum())
+    eps = 1e-6
+    for arr, grad, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+        for idx in [(0, 0, 0, 0), (0, 0, N - 1, d - 1), (0, arr.shape[1] - 1, 2, 1)]:
+            plus, minus = [a.copy() for a in (q, k, v)], [a.copy() for a in (q, k, v)]
+            plus[which][idx] += eps
+            minus[which][idx] -= eps
+            fd = (loss(*plus) - loss(*minus)) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-7
+
+
+def test_backward_invariants_key_sums():
+    B, Hq, Hkv, N, d, scale = 1, 4, 2, 17, 8, 0.3
+    q, k, v, do = rnd((B, Hq, N, d), 200), rnd((B, Hkv, N, d), 201), rnd((B, Hkv, N, d), 202), rnd((B, Hq, N, d), 203)
+    dq, dk, dv = ao.sdpa_backward_ref(q, k, v, do, scale, True)
+    # rows of dS sum to zero, so the key gradients of a head group sum to zero
+    assert np.abs(dk.sum(axis=2)).max() <= 1e-12
+    # rows of P sum to one, so the value gradients sum to the output gradients of the group
+    want = do.reshape(B, Hkv, Hq // Hkv, N, d).sum(axis=(2, 3))
+    assert np.abs(dv.sum(axis=2) - want).max() <= 1e-12
+
+
 # ------------------------------------------------------------ chunk after a cached prefix
 
 def test_position_mask_matches_printed_example():
