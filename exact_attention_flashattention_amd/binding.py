@@ -39,6 +39,9 @@ SIGNATURES = [
     ("attn_kv_append", _i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
     ("attn_prefill_paged", _i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                                 _i, _i, _f, _var, _vp]),
+    ("attn_backward_workspace_size", _sz, [_i, _i, _i]),
+    ("attn_backward", _i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp,
+                           _sz, _vp]),
     ("attn_gather_pages", _i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
     ("attn_status_string", ctypes.c_char_p, [_i]),
     ("attn_version", _i, []),
@@ -310,6 +313,45 @@ def attn_prefill_paged(q, k_pages, v_pages, block_table, cu_q, seq_lens, o=None,
                                   float(d ** -0.5 if scale is None else scale), var, _stream(stream))
     _check(st, "attn_prefill_paged")
     return o
+
+
+def attn_backward_workspace_size(B: int, N: int, Hq: int) -> int:
+    return int(lib().attn_backward_workspace_size(B, N, Hq))
+
+
+def attn_backward(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, *, causal: bool = True,
+                  scale: Optional[float] = None, layout: str = "BNHD", workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of the bf16 prefill given dout; o and lse
+    ([B, Hq, N] fp32) are the forward's outputs. Returns (dq, dk, dv)."""
+    import torch
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {list(LAYOUTS)}")
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        if t.dtype != torch.bfloat16 or t.dim() != 4:
+            raise ValueError(f"{n} must be a bf16 4-D tensor")
+    if o.shape != q.shape or dout.shape != q.shape or v.shape != k.shape:
+        raise ValueError("o and dout must match q, v must match k")
+    if layout == "BNHD":
+        B, N, Hq, d = q.shape
+        Hkv = k.shape[2]
+    else:
+        B, Hq, N, d = q.shape
+        Hkv = k.shape[1]
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("lse must be float32 [B, Hq, N]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = attn_backward_workspace_size(B, N, Hq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+    st = lib().attn_backward(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _dev(dout, "dout"),
+                             _dev(lse, "lse"), _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"), B, N, Hq,
+                             Hkv, d, float(d ** -0.5 if scale is None else scale), int(bool(causal)),
+                             LAYOUTS[layout], _dev(workspace, "workspace"),
+                             workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "attn_backward")
+    return dq, dk, dv
 
 
 def attn_gather_pages(pages, block_table, seq_lens, max_len: int, out=None, stream=None):

@@ -242,6 +242,53 @@ int attn_prefill_paged(const void* q, const void* k_pages, const void* v_pages,
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+size_t attn_backward_workspace_size(int B, int N, int Hq) {
+  if (B < 1 || N < 1 || Hq < 1) return 0;
+  const long long npad = ((long long)N + 63) / 64 * 64;
+  return (size_t)(2LL * B * Hq * npad * 4);
+}
+
+int attn_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, int B, int N, int Hq, int Hkv, int d,
+                  float scale, int causal, int layout, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL;
+  if (B < 1 || N < 1) return ATTN_ERR_SHAPE;
+  int st = check_heads(Hq, Hkv);
+  if (st) return st;
+  if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  if (layout != ATTN_BNHD && layout != ATTN_BHND) return ATTN_ERR_LAYOUT;
+  if (!isfinite(scale)) return ATTN_ERR_SHAPE;
+  if ((long long)B * N * Hq * d > kMaxElems) return ATTN_ERR_SHAPE;
+  if ((long long)Hq * d >= (1 << 24)) return ATTN_ERR_SHAPE;  // row offsets in a tile fit 32 bits
+  const size_t need = attn_backward_workspace_size(B, N, Hq);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return ATTN_ERR_ALIGN;
+
+  attn::BwdParams p = {};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
+  p.dq = dq; p.dk = dk; p.dv = dv;
+  p.B = B; p.N = N; p.Npad = (N + 63) / 64 * 64; p.Hq = Hq; p.Hkv = Hkv;
+  p.dvec = static_cast<float*>(workspace);
+  p.lse2 = p.dvec + (size_t)B * Hq * p.Npad;
+  const long long D = d;
+  if (layout == ATTN_BNHD) {
+    p.q_sb = (long long)N * Hq * D; p.q_sn = Hq * D; p.q_sh = D;
+    p.k_sb = (long long)N * Hkv * D; p.k_sn = Hkv * D; p.k_sh = D;
+  } else {
+    p.q_sb = (long long)Hq * N * D; p.q_sn = D; p.q_sh = (long long)N * D;
+    p.k_sb = (long long)Hkv * N * D; p.k_sn = D; p.k_sh = (long long)N * D;
+  }
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.causal = causal ? 1 : 0;
+  const hipError_t e = attn::launch_backward(p, d, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 int attn_gather_pages(const void* pages, const int32_t* block_table, const int32_t* seq_lens,
                       void* out, int B, int Hkv, int d, int page_size, int max_pages_per_seq,
                       int num_pages, int max_len, int elem_bytes, void* stream) {

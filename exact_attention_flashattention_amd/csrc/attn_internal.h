@@ -56,7 +56,31 @@ struct DecodeParams {
   const float* sinks;
 };
 
+// Backward of the prefill (bf16). q, o, dout, dq share q's strides; k, v,
+// dk, dv share k's. lse is the forward's [B, Hq, N] natural-log LSE; dvec and
+// lse2 are workspace arrays [B, Hq, Npad] (Npad = N rounded up to 64).
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dvec;
+  float* lse2;
+  int B, N, Npad, Hq, Hkv;
+  long long q_sb, q_sn, q_sh;
+  long long k_sb, k_sn, k_sh;
+  float scale;
+  float scale_log2;
+  int causal;
+};
+
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream);
+hipError_t launch_backward(const BwdParams& p, int d, hipStream_t stream);
 hipError_t launch_prefill_paged(const PrefillParams& p, int d, int max_q_len, hipStream_t stream);
 hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
                             const int32_t* block_table, const int32_t* cu_new,

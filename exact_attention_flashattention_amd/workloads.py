@@ -100,6 +100,13 @@ def prefill_inputs(B: int, N: int, Hq: int, Hkv: int, d: int, *, seed: int,
                          causal, layout, name)
 
 
+def output_gradient(x: PrefillInputs, *, seed: int) -> torch.Tensor:
+    """dL/do for a backward pass: i.i.d. N(0, 1) of q's shape and dtype, from
+    its own generator (seeded separately, so the forward inputs are unchanged)."""
+    g = _gen(seed)
+    return _randn(g, tuple(x.q.shape), x.q.dtype)
+
+
 def paged_decode_inputs(B: int, Hq: int, Hkv: int, d: int, seq_lens, *, seed: int,
                         page_size: int = PAGE_SIZE, permute: bool = True,
                         max_pages_per_seq: Optional[int] = None,

@@ -9,6 +9,7 @@
  *   attn_decode : one new query token per sequence against a KV cache stored in
  *       fixed-size pages addressed through a block table, split along the
  *       context and merged by log-sum-exp.
+ *   attn_backward : the gradients of the prefill with respect to q, k and v.
  *   attn_prefill_paged : a chunk of new queries per sequence against the same
  *       paged cache, each row seeing every key up to its own position (the
  *       attention half of chunked prefill); attn_kv_append writes the chunk's
@@ -284,6 +285,38 @@ int attn_decode_ex(const void* q, const void* k_pages, const void* v_pages,
                    int B, int Hq, int Hkv, int d, int page_size, int max_pages_per_seq,
                    int num_pages, float scale, int num_splits, const attn_variant* variant,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_backward_workspace_size - bytes of fp32 scratch attn_backward needs:
+ * two [B, Hq, Npad] arrays, Npad = N rounded up to a multiple of 64.
+ * Returns 0 for invalid sizes.
+ */
+size_t attn_backward_workspace_size(int B, int N, int Hq);
+
+/*
+ * attn_backward - gradients of attn_prefill_ex's output with respect to q, k
+ * and v, bf16 in and out, fp32 accumulation. S and P are recomputed tile by
+ * tile from the forward's log-sum-exp instead of being stored ("inference-
+ * attention", section "FlashAttention"):
+ *   dV = P^T dO, dP = dO V^T, D = rowsum(dO * O), dS = P * (dP - D),
+ *   dQ = scale * dS K, dK = scale * dS^T Q,
+ * where dK, dV of a KV head sum over its g query heads (GQA, [SDPA] section 6).
+ *
+ * q, o, dout, dq: [B, N, Hq, d] (layout ATTN_BNHD) or [B, Hq, N, d] (ATTN_BHND);
+ * k, v, dk, dv:   the same layout with Hkv heads.
+ * o, lse:         the forward's output and its fp32 [B, Hq, N] natural-log LSE
+ *                 (attn_prefill_ex with the same q, k, v, scale, causal).
+ * dq, dk, dv:     outputs, fully overwritten (no accumulation into them).
+ * workspace:      caller-owned device memory of at least
+ *                 attn_backward_workspace_size(B, N, Hq) bytes; calls that
+ *                 overlap in time must not share one.
+ * Requires d in {64, 128} and Hq a multiple of Hkv. Deterministic: every
+ * gradient element is reduced in a fixed order (no atomics).
+ */
+int attn_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, int B, int N, int Hq, int Hkv, int d,
+                  float scale, int causal, int layout, void* workspace, size_t workspace_bytes,
+                  void* stream);
 
 /*
  * attn_gather_pages - materialise the logical cache of each sequence from the

@@ -32,7 +32,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) == 11
+    assert len(names) == 13
     for n in names:
         assert hasattr(L, n), n
     assert sorted(n for n, _, _ in binding.SIGNATURES) == names
@@ -187,6 +187,32 @@ def test_prefill_paged_rejects(L, kw, err):
 def test_prefill_paged_with_no_rows_is_a_no_op(L):
     assert paged(L, total=0) == 0
     assert paged(L, max_q=0) == 0
+
+
+def backward(L, **kw):
+    a = dict(q=A, k=A, v=A, o=A, do=A, lse=A, dq=A, dk=A, dv=A, B=1, N=8, Hq=4, Hkv=2, d=64, scale=0.125,
+             causal=1, layout=0, ws=A, ws_bytes=1 << 20)
+    a.update(kw)
+    return L.attn_backward(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["B"],
+                           a["N"], a["Hq"], a["Hkv"], a["d"], a["scale"], a["causal"], a["layout"], a["ws"],
+                           a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,err", [
+    (dict(do=None), "ATTN_ERR_NULL"), (dict(lse=None), "ATTN_ERR_NULL"), (dict(dv=None), "ATTN_ERR_NULL"),
+    (dict(B=0), "ATTN_ERR_SHAPE"), (dict(N=0), "ATTN_ERR_SHAPE"), (dict(Hq=4, Hkv=3), "ATTN_ERR_GQA"),
+    (dict(d=80), "ATTN_ERR_HEAD_DIM"), (dict(layout=5), "ATTN_ERR_LAYOUT"), (dict(scale=float("nan")), "ATTN_ERR_SHAPE"),
+    (dict(ws=None), "ATTN_ERR_WORKSPACE"), (dict(ws_bytes=8), "ATTN_ERR_WORKSPACE"), (dict(dk=A + 8), "ATTN_ERR_ALIGN"),
+    (dict(lse=A + 2), "ATTN_ERR_ALIGN"),
+])
+def test_backward_rejects(L, kw, err):
+    assert backward(L, **kw) == ERR[err]
+
+
+def test_backward_workspace_size(L):
+    assert L.attn_backward_workspace_size(2, 100, 8) == 2 * 2 * 8 * 128 * 4
+    assert L.attn_backward_workspace_size(1, 64, 1) == 2 * 64 * 4
+    assert L.attn_backward_workspace_size(0, 64, 1) == 0
 
 
 def test_binding_refuses_cpu_tensors():
