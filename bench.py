@@ -21,7 +21,9 @@ prefill in TFLOP/s (visible (query, key) pairs, 4 d flops each). "variants"
 reports the headline prefill with a 1024-token window, 4 initial tokens and
 per-head sink logits (TFLOP/s over the visible pairs), and the long-context
 decode with an 8192-token window, 4 initial tokens and sink logits (GB/s over
-the K/V bytes of the visible tokens).
+the K/V bytes of the visible tokens). "backward" reports dq, dk, dv of the
+headline prefill given an output gradient (TFLOP/s over 5 products of 2 d
+flops per visible pair, 2.5 times the forward count).
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -243,6 +245,38 @@ def variants_report(dev, stream, steps: int) -> dict:
     }
 
 
+def backward_setup(dev, stream):
+    """The headline prefill's inputs, its forward output and LSE, an output
+    gradient, and the backward call."""
+    import torch
+    import exact_attention_flashattention_amd as pkg
+    from exact_attention_flashattention_amd import workloads as wl
+    x = wl.workload_2()
+    q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
+    do = wl.output_gradient(x, seed=49).to(dev)
+    lse = torch.empty((x.B, x.Hq, x.N), dtype=torch.float32, device=dev)
+    o = pkg.attn_prefill_ex(q, k, v, scale=x.scale, lse=lse, stream=stream)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(pkg.attn_backward_workspace_size(x.B, x.N, x.Hq) // 4 + 4, dtype=torch.float32, device=dev)
+    fn = lambda: pkg.attn_backward(q, k, v, o, do, lse, dq, dk, dv, scale=x.scale, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    return x, fn
+
+
+def backward_report(dev, stream, steps: int) -> dict:
+    """dq, dk, dv of the headline prefill, timed apart from the step."""
+    x, fn = backward_setup(dev, stream)
+    t = time_calls(fn, stream, 3, steps)
+    fl = 5 * causal_flops(x.B, x.Hq, x.N, x.d) // 2   # 5 products of 2 d flops per visible pair
+    tf = fl / (t * 1e-6) / 1e12
+    log(f"backward: {t:.1f} us ({tf:.1f} TFLOP/s)")
+    return {"workload": f"{x.name}, dq/dk/dv given dO", "value": round(tf, 3), "unit": "TFLOP/s",
+            "avg_call_us": round(t, 2), "flops_per_call": fl,
+            "kernels": "bwd_pre_kernel<128> + bwd_dkdv_kernel<128,4,64> + bwd_dq_kernel<128,8,64>",
+            "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / BF16_PEAK_TFLOPS, 4)}}
+
+
 PREFILL_SOURCES = ["prefill_bf16.hip", "attn_internal.h"]
 DECODE_SOURCES = ["decode.hip", "attn_internal.h"]
 APPEND_SOURCES = ["kv_append.hip", "attn_internal.h"]
@@ -314,6 +348,9 @@ def only(args, dev) -> int:
         o = torch.empty_like(q)
         fn = lambda: pkg.attn_prefill(q, k, v, o, scale=x.scale, stream=stream)
         work = {"flops_per_launch": causal_flops(x.B, x.Hq, x.N, x.d)}
+    elif args.only == "backward":
+        x, fn = backward_setup(dev, stream)
+        work = {"flops_per_call": 5 * causal_flops(x.B, x.Hq, x.N, x.d) // 2}
     elif args.only in ("chunked", "append"):
         x, append, attend = chunked_setup(dev, stream)
         fn = attend if args.only == "chunked" else append
@@ -344,7 +381,7 @@ def only(args, dev) -> int:
     b.record(stream)
     torch.cuda.synchronize()
     srcs = {"prefill": PREFILL_SOURCES, "decode": DECODE_SOURCES, "chunked": PREFILL_SOURCES,
-            "append": APPEND_SOURCES}.get(args.only)
+            "append": APPEND_SOURCES, "backward": ["backward_bf16.hip", "attn_internal.h", "cdna4.h"]}.get(args.only)
     print(json.dumps({"only": args.only, "steps": args.steps,
                       "avg_us": round(a.elapsed_time(b) * 1e3 / args.steps, 2),
                       "source_sha256": source_hash(*srcs) if srcs else None, **work}), flush=True)
@@ -361,7 +398,7 @@ def main() -> int:
                     help="skip the chunked-prefill (KV append + paged prefill) and variant reports")
     ap.add_argument("--cpu-batches", type=int, default=2,
                     help="batch entries of the headline prefill the CPU oracle is timed on")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy", "chunked", "append"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "copy", "chunked", "append", "backward"], default=None,
                     help="launch only this kernel (for counter runs under rocprofv3); "
                          "'copy' is a plain 1 GiB device copy used to calibrate byte counters")
     ap.add_argument("--write-traffic", metavar="DIR", default=None,
@@ -478,11 +515,13 @@ def main() -> int:
         },
         "chunked_prefill": None,
         "variants": None,
+        "backward": None,
         "cpu_baseline": None,
     }
     if not args.no_chunked:
         result["chunked_prefill"] = chunked_report(dev, stream, max(10, args.steps // 2))
         result["variants"] = variants_report(dev, stream, max(10, args.steps // 2))
+        result["backward"] = backward_report(dev, stream, max(10, args.steps // 5))
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(x2, x5, args.cpu_batches)
