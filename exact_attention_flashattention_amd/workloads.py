@@ -250,6 +250,62 @@ def poison_chunk_slots(x: ChunkInputs, value: float = float("nan")) -> None:
     x.v_pages[~keep] = value
 
 
+@dataclasses.dataclass
+class MlaDecodeInputs:
+    """One decode step of absorbed multi-head latent attention: every token
+    caches one row [latent (d_c) ; rotary key (d_r)] shared by all heads."""
+    q: torch.Tensor            # [B, Hq, d_c + d_r]
+    kv_pages: torch.Tensor     # [num_pages, page_size, d_c + d_r]
+    block_table: torch.Tensor  # int32 [B, max_pages_per_seq]
+    seq_lens: torch.Tensor     # int32 [B]
+    B: int
+    Hq: int
+    d_c: int
+    d_r: int
+    page_size: int
+    max_pages_per_seq: int
+    scale: float
+    name: str = ""
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.kv_pages.shape[0])
+
+
+def mla_decode_inputs(B: int, Hq: int, d_c: int, d_r: int, seq_lens, *, seed: int,
+                      page_size: int = PAGE_SIZE, permute: bool = True,
+                      max_pages_per_seq: Optional[int] = None, dtype: torch.dtype = torch.bfloat16,
+                      scale: Optional[float] = None, d_head: int = 128, name: str = "") -> MlaDecodeInputs:
+    """Draw an absorbed-MLA decode problem: q, then (for a range) the lengths,
+    then the cache rows and the page permutation, as for paged_decode_inputs.
+    The default scale is 1 / sqrt(d_head + d_r), the score scale of the
+    non-absorbed heads the latent stands for."""
+    g = _gen(seed)
+    dk = d_c + d_r
+    q = _randn(g, (B, Hq, dk), dtype)
+    if isinstance(seq_lens, tuple):
+        lo, hi = seq_lens
+        lens = torch.randint(lo, hi + 1, (B,), generator=g, dtype=torch.int64).tolist()
+    else:
+        lens = [int(x) for x in seq_lens]
+        assert len(lens) == B
+    pages_per = [-(-L // page_size) for L in lens]
+    total = max(sum(pages_per), 1)
+    mpps = max(1, max(pages_per)) if max_pages_per_seq is None else max_pages_per_seq
+    assert mpps >= max(pages_per, default=0)
+    kv = _randn(g, (total, page_size, dk), dtype)
+    order = torch.randperm(total, generator=g).tolist() if permute else list(range(total))
+    table = torch.full((B, mpps), -1, dtype=torch.int32)
+    cursor = 0
+    for b in range(B):
+        n = pages_per[b]
+        if n:
+            table[b, :n] = torch.tensor(order[cursor:cursor + n], dtype=torch.int32)
+        cursor += n
+    return MlaDecodeInputs(q, kv, table, torch.tensor(lens, dtype=torch.int32), B, Hq, d_c, d_r, page_size,
+                           mpps, 1.0 / math.sqrt(d_head + d_r) if scale is None else scale, name)
+
+
 def poison_unused_slots(x: DecodeInputs, value: float = float("nan")) -> None:
     """Fill the slots past each sequence's end on its last page with ``value``
     (and any pool page no sequence references). A correct kernel never lets
@@ -270,7 +326,8 @@ def poison_unused_slots(x: DecodeInputs, value: float = float("nan")) -> None:
 
 # The standard workloads. Index 1 is the small fp32 parity case; index 2 is
 # the headline prefill; index 3 the MHA/MQA endpoints; 4 and 5 decode; 6 a
-# chunk of new tokens after a long cached prefix (paged prefill + append).
+# chunk of new tokens after a long cached prefix (paged prefill + append); 7
+# an absorbed-MLA decode (one shared 576-wide latent row per token).
 
 def workload_1() -> PrefillInputs:
     return prefill_inputs(1, 128, 4, 2, 64, seed=43, dtype=torch.float32,
@@ -304,3 +361,9 @@ def workload_6() -> ChunkInputs:
     return chunked_prefill_inputs(4, 32, 8, 128, (6144, 14336), [2048] * 4, seed=48,
                                   name="chunked prefill bf16 B=4 Hq=32 Hkv=8 d=128 prefix~U[6144,14336] "
                                        "chunk=2048 page=16 permuted")
+
+
+def workload_7() -> MlaDecodeInputs:
+    return mla_decode_inputs(4, 128, 512, 64, (16384, 32768), seed=49,
+                             name="MLA-absorbed decode bf16 B=4 Hq=128 d_c=512 d_r=64 "
+                                  "seq_lens~U[16384,32768] page=16 permuted")

@@ -108,7 +108,7 @@ def group_check(x: wl.PrefillInputs, dout, b: int, kvh: int):
 
 def test_workload_2_shape_full_head_group():
     x = wl.workload_2()
-    dout = wl.output_gradient(x, seed=49)
+    dout = wl.output_gradient(x, seed=144)
     log(f"case: {x.name}, head group (b=3, kv head 5)")
     group_check(x, dout, 3, 5)
 
@@ -116,6 +116,6 @@ def test_workload_2_shape_full_head_group():
 @pytest.mark.parametrize("hkv", [16, 1])
 def test_workload_3_shape_full_head_group(hkv):
     x = wl.workload_3(hkv)
-    dout = wl.output_gradient(x, seed=50)
+    dout = wl.output_gradient(x, seed=145)
     log(f"case: {x.name}, head group (b=6, kv head {hkv - 1})")
     group_check(x, dout, 6, hkv - 1)

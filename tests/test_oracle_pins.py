@@ -558,6 +558,59 @@ def test_windowed_decode_is_the_last_row_of_the_windowed_prefill():
             assert np.abs(dec - o[:, :, t]).max() <= 1e-12
 
 
+# ------------------------------------------------------------ MLA absorbed decode
+
+def test_mla_absorbed_equals_recomputed_keys_and_values():
+    """The pages' own check: attention over the latent with W_UK absorbed into
+    the query and W_UV applied to the latent output equals ordinary attention
+    with every head's keys [W_UK c_t ; k^R_t] and values W_UV c_t recomputed."""
+    rng = np.random.default_rng(210)
+    H, D, d_c, d_r, L, scale = 4, 6, 10, 3, 13, 0.3
+    c = rng.standard_normal((L, d_c))
+    kr = rng.standard_normal((L, d_r))
+    W_uk = rng.standard_normal((H, D, d_c))
+    W_uv = rng.standard_normal((H, D, d_c))
+    q_nope = rng.standard_normal((H, D))
+    q_rope = rng.standard_normal((H, d_r))
+    # recomputed keys and values, plain softmax attention per head
+    want = np.zeros((H, D))
+    for h in range(H):
+        k = np.concatenate([c @ W_uk[h].T, kr], axis=1)        # [L, D + d_r]
+        v = c @ W_uv[h].T                                        # [L, D]
+        s = k @ np.concatenate([q_nope[h], q_rope[h]]) * scale
+        p = np.exp(s - s.max())
+        want[h] = (p / p.sum()) @ v
+    # absorbed: one shared latent row per token, in 4-token pages (permuted)
+    q_abs = np.concatenate([np.einsum("hdc,hd->hc", W_uk, q_nope), q_rope], axis=1)[None]
+    rows = np.concatenate([c, kr], axis=1)
+    n_pages = ao.pages_needed(L, 4)
+    perm = rng.permutation(n_pages + 2)[:n_pages]
+    pool = np.full((n_pages + 2, 4, d_c + d_r), np.nan)
+    for t in range(L):
+        pool[perm[t // 4], t % 4] = rows[t]
+    o_lat = ao.mla_decode_ref(q_abs, pool, perm[None], np.array([L]), scale, d_c)[0]
+    got = np.einsum("hdc,hc->hd", W_uv, o_lat)
+    assert np.abs(got - want).max() <= 1e-10
+
+
+def test_mla_decode_is_mqa_with_shared_value_columns():
+    rng = np.random.default_rng(220)
+    B, Hq, d_c, d_r, ps = 2, 8, 12, 4, 4
+    lens = [9, 16]
+    q = rng.standard_normal((B, Hq, d_c + d_r))
+    n = [ao.pages_needed(L, ps) for L in lens]
+    pool = rng.standard_normal((sum(n), ps, d_c + d_r))
+    table = np.array([[0, 1, 2, -1], [3, 4, 5, 6]])
+    got = ao.mla_decode_ref(q, pool, table, np.array(lens), 0.25, d_c)
+    for b in range(B):
+        rows = torch.from_numpy(np.concatenate([pool[p] for p in table[b, :n[b]]])[:lens[b]])
+        k = rows[None, None]                    # one KV head
+        v = rows[None, None, :, :d_c]
+        want = F.scaled_dot_product_attention(torch.from_numpy(q[b])[None, :, None], k, v, scale=0.25,
+                                              enable_gqa=True)[0, :, 0]
+        assert np.abs(got[b] - want.numpy()).max() <= 1e-12
+
+
 # ------------------------------------------------------------ cache sizing
 
 def test_kv_cache_bytes_matches_printed_values():
