@@ -23,7 +23,9 @@ per-head sink logits (TFLOP/s over the visible pairs), and the long-context
 decode with an 8192-token window, 4 initial tokens and sink logits (GB/s over
 the K/V bytes of the visible tokens). "backward" reports dq, dk, dv of the
 headline prefill given an output gradient (TFLOP/s over 5 products of 2 d
-flops per visible pair, 2.5 times the forward count).
+flops per visible pair, 2.5 times the forward count). "mla_decode" reports
+the absorbed multi-head latent attention decode (B=16, Hq=128, 576-wide latent
+rows, L ~ U[8192, 16384]) in GB/s over the latent rows read once.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -277,6 +279,38 @@ def backward_report(dev, stream, steps: int) -> dict:
                          "frac": round(tf / BF16_PEAK_TFLOPS, 4)}}
 
 
+def mla_setup(dev, stream):
+    import torch
+    import exact_attention_flashattention_amd as pkg
+    from exact_attention_flashattention_amd import workloads as wl
+    x = wl.workload_7()
+    q, kv, bt, sl = (t.to(dev) for t in (x.q, x.kv_pages, x.block_table, x.seq_lens))
+    o = torch.empty((x.B, x.Hq, x.d_c), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(pkg.attn_decode_mla_workspace_size(x.B, x.Hq, x.max_pages_per_seq, 0) // 4 + 4,
+                     dtype=torch.float32, device=dev)
+    fn = lambda: pkg.attn_decode_mla(q, kv, bt, sl, o, scale=x.scale, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    return x, fn
+
+
+def mla_report(dev, stream, steps: int) -> dict:
+    """Absorbed-MLA decode: latent rows read once (K and V share them)."""
+    import exact_attention_flashattention_amd as pkg
+    x, fn = mla_setup(dev, stream)
+    t = time_calls(fn, stream, 3, steps)
+    by = int(x.seq_lens.sum()) * (x.d_c + x.d_r) * 2
+    gb = by / (t * 1e-6) / 1e9
+    fl = int(x.seq_lens.sum()) * x.Hq * 2 * (2 * x.d_c + x.d_r)
+    log(f"mla decode: {t:.1f} us ({gb:.0f} GB/s, {fl / (t * 1e-6) / 1e12:.1f} TFLOP/s)")
+    return {"workload": x.name, "seq_lens": x.seq_lens.tolist(),
+            "splits": pkg.attn_decode_mla_num_splits(x.B, x.Hq, x.max_pages_per_seq, 0),
+            "value": round(gb, 2), "unit": "GB/s", "avg_call_us": round(t, 2), "kv_bytes_per_call": by,
+            "tflops": round(fl / (t * 1e-6) / 1e12, 3),
+            "kernels": "mla_split_kernel + mla_merge_kernel",
+            "roofline": {"bound": "hbm", "achieved": round(gb, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gb / HBM_PEAK_GBS, 4)}}
+
+
 PREFILL_SOURCES = ["prefill_bf16.hip", "attn_internal.h"]
 DECODE_SOURCES = ["decode.hip", "attn_internal.h"]
 APPEND_SOURCES = ["kv_append.hip", "attn_internal.h"]
@@ -348,6 +382,9 @@ def only(args, dev) -> int:
         o = torch.empty_like(q)
         fn = lambda: pkg.attn_prefill(q, k, v, o, scale=x.scale, stream=stream)
         work = {"flops_per_launch": causal_flops(x.B, x.Hq, x.N, x.d)}
+    elif args.only == "mla":
+        x, fn = mla_setup(dev, stream)
+        work = {"kv_bytes_per_call": int(x.seq_lens.sum()) * (x.d_c + x.d_r) * 2}
     elif args.only == "backward":
         x, fn = backward_setup(dev, stream)
         work = {"flops_per_call": 5 * causal_flops(x.B, x.Hq, x.N, x.d) // 2}
@@ -381,7 +418,8 @@ def only(args, dev) -> int:
     b.record(stream)
     torch.cuda.synchronize()
     srcs = {"prefill": PREFILL_SOURCES, "decode": DECODE_SOURCES, "chunked": PREFILL_SOURCES,
-            "append": APPEND_SOURCES, "backward": ["backward_bf16.hip", "attn_internal.h", "cdna4.h"]}.get(args.only)
+            "append": APPEND_SOURCES, "backward": ["backward_bf16.hip", "attn_internal.h", "cdna4.h"],
+            "mla": ["decode_mla.hip", "attn_internal.h", "cdna4.h"]}.get(args.only)
     print(json.dumps({"only": args.only, "steps": args.steps,
                       "avg_us": round(a.elapsed_time(b) * 1e3 / args.steps, 2),
                       "source_sha256": source_hash(*srcs) if srcs else None, **work}), flush=True)
@@ -398,7 +436,8 @@ def main() -> int:
                     help="skip the chunked-prefill (KV append + paged prefill) and variant reports")
     ap.add_argument("--cpu-batches", type=int, default=2,
                     help="batch entries of the headline prefill the CPU oracle is timed on")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy", "chunked", "append", "backward"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "copy", "chunked", "append", "backward", "mla"],
+                    default=None,
                     help="launch only this kernel (for counter runs under rocprofv3); "
                          "'copy' is a plain 1 GiB device copy used to calibrate byte counters")
     ap.add_argument("--write-traffic", metavar="DIR", default=None,
@@ -516,12 +555,14 @@ def main() -> int:
         "chunked_prefill": None,
         "variants": None,
         "backward": None,
+        "mla_decode": None,
         "cpu_baseline": None,
     }
     if not args.no_chunked:
         result["chunked_prefill"] = chunked_report(dev, stream, max(10, args.steps // 2))
         result["variants"] = variants_report(dev, stream, max(10, args.steps // 2))
         result["backward"] = backward_report(dev, stream, max(10, args.steps // 5))
+        result["mla_decode"] = mla_report(dev, stream, max(10, args.steps // 2))
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(x2, x5, args.cpu_batches)

@@ -42,6 +42,9 @@ SIGNATURES = [
     ("attn_backward_workspace_size", _sz, [_i, _i, _i]),
     ("attn_backward", _i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp,
                            _sz, _vp]),
+    ("attn_decode_mla_num_splits", _i, [_i, _i, _i, _i]),
+    ("attn_decode_mla_workspace_size", _sz, [_i, _i, _i, _i]),
+    ("attn_decode_mla", _i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
     ("attn_gather_pages", _i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
     ("attn_status_string", ctypes.c_char_p, [_i]),
     ("attn_version", _i, []),
@@ -352,6 +355,44 @@ def attn_backward(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, *, causal: b
                              workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "attn_backward")
     return dq, dk, dv
+
+
+def attn_decode_mla_num_splits(B: int, Hq: int, max_pages_per_seq: int, num_splits: int = 0) -> int:
+    s = lib().attn_decode_mla_num_splits(B, Hq, max_pages_per_seq, num_splits)
+    _check(min(s, 0), "attn_decode_mla_num_splits")
+    return s
+
+
+def attn_decode_mla_workspace_size(B: int, Hq: int, max_pages_per_seq: int, num_splits: int = 0) -> int:
+    return int(lib().attn_decode_mla_workspace_size(B, Hq, max_pages_per_seq, num_splits))
+
+
+def attn_decode_mla(q, kv_pages, block_table, seq_lens, o=None, *, scale: Optional[float] = None,
+                    d_c: int = 512, num_splits: int = 0, workspace=None, stream=None):
+    """Absorbed-MLA decode. q [B, Hq, 576] bf16; kv_pages [num_pages, 16, 576]
+    bf16; returns o [B, Hq, 512]. The default scale is 1/sqrt(128 + 64)."""
+    import torch
+    if q.dtype != torch.bfloat16 or kv_pages.dtype != torch.bfloat16:
+        raise ValueError("q and kv_pages must be bf16")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    B, Hq, dk = q.shape
+    num_pages, page_size, dk2 = kv_pages.shape
+    if dk2 != dk:
+        raise ValueError("q and kv_pages disagree on the row width")
+    mpps = block_table.shape[1]
+    if o is None:
+        o = torch.empty((B, Hq, d_c), dtype=q.dtype, device=q.device)
+    need = attn_decode_mla_workspace_size(B, Hq, mpps, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+    st = lib().attn_decode_mla(_dev(q, "q"), _dev(kv_pages, "kv_pages"), _dev(block_table, "block_table"),
+                               _dev(seq_lens, "seq_lens"), _dev(o, "o"), B, Hq, d_c, dk - d_c, page_size, mpps,
+                               num_pages, float((128 + 64) ** -0.5 if scale is None else scale), num_splits,
+                               _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                               _stream(stream))
+    _check(st, "attn_decode_mla")
+    return o
 
 
 def attn_gather_pages(pages, block_table, seq_lens, max_len: int, out=None, stream=None):

@@ -289,6 +289,49 @@ int attn_backward(const void* q, const void* k, const void* v, const void* o, co
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+int attn_decode_mla_num_splits(int B, int Hq, int max_pages_per_seq, int num_splits) {
+  if (B < 1 || Hq < 1 || max_pages_per_seq < 1 || num_splits < 0) return ATTN_ERR_SHAPE;
+  const int cap = max_pages_per_seq < 1024 ? max_pages_per_seq : 1024;
+  int s = num_splits > 0 ? num_splits : attn::mla_auto_splits(B, Hq, max_pages_per_seq);
+  if (s > cap) s = cap;
+  return s < 1 ? 1 : s;
+}
+
+size_t attn_decode_mla_workspace_size(int B, int Hq, int max_pages_per_seq, int num_splits) {
+  const int S = attn_decode_mla_num_splits(B, Hq, max_pages_per_seq, num_splits);
+  if (S < 1 || Hq % 16) return 0;
+  return (size_t)B * Hq * S * (512 + 2) * 4;
+}
+
+int attn_decode_mla(const void* q, const void* kv_pages, const int32_t* block_table, const int32_t* seq_lens,
+                    void* o, int B, int Hq, int d_c, int d_r, int page_size, int max_pages_per_seq,
+                    int num_pages, float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (!q || !kv_pages || !block_table || !seq_lens || !o) return ATTN_ERR_NULL;
+  if (B < 1 || Hq < 1 || max_pages_per_seq < 1 || num_pages < 1 || num_splits < 0) return ATTN_ERR_SHAPE;
+  if (Hq % 16) return ATTN_ERR_SHAPE;
+  if (d_c != 512 || d_r != 64) return ATTN_ERR_HEAD_DIM;
+  if (page_size != 16) return ATTN_ERR_PAGE;
+  if (!isfinite(scale)) return ATTN_ERR_SHAPE;
+  if ((long long)max_pages_per_seq * page_size > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  if ((long long)num_pages * page_size * 576 > kMaxElems || (long long)B * max_pages_per_seq > kMaxElems)
+    return ATTN_ERR_SHAPE;
+  const int S = attn_decode_mla_num_splits(B, Hq, max_pages_per_seq, num_splits);
+  if (!workspace || workspace_bytes < attn_decode_mla_workspace_size(B, Hq, max_pages_per_seq, num_splits))
+    return ATTN_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(kv_pages) || !aligned16(o) || !aligned16(workspace) ||
+      (reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return ATTN_ERR_ALIGN;
+  attn::MlaParams p = {};
+  p.q = q; p.kv_pages = kv_pages; p.block_table = block_table; p.seq_lens = seq_lens; p.o = o;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_ml = p.ws_o + (size_t)B * Hq * S * 512;
+  p.B = B; p.Hq = Hq; p.max_pages_per_seq = max_pages_per_seq; p.num_splits = S;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  const hipError_t e = attn::launch_decode_mla(p, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 int attn_gather_pages(const void* pages, const int32_t* block_table, const int32_t* seq_lens,
                       void* out, int B, int Hkv, int d, int page_size, int max_pages_per_seq,
                       int num_pages, int max_len, int elem_bytes, void* stream) {

@@ -79,6 +79,23 @@ struct BwdParams {
   int causal;
 };
 
+// Absorbed-MLA decode: q [B, Hq, 576], pool [pages, 16, 576] (latent 512 then
+// rotary key 64), o [B, Hq, 512]; workspace as for decode with d = 512.
+struct MlaParams {
+  const void* q;
+  const void* kv_pages;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* o;
+  float* ws_ml;  // [B, Hq, splits, 2]
+  float* ws_o;   // [B, Hq, splits, 512]
+  int B, Hq, max_pages_per_seq, num_splits;
+  float scale_log2;
+};
+
+hipError_t launch_decode_mla(const MlaParams& p, hipStream_t stream);
+int mla_auto_splits(int B, int Hq, int max_pages_per_seq);
+
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream);
 hipError_t launch_backward(const BwdParams& p, int d, hipStream_t stream);
 hipError_t launch_prefill_paged(const PrefillParams& p, int d, int max_q_len, hipStream_t stream);

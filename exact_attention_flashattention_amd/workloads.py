@@ -306,6 +306,20 @@ def mla_decode_inputs(B: int, Hq: int, d_c: int, d_r: int, seq_lens, *, seed: in
                            mpps, 1.0 / math.sqrt(d_head + d_r) if scale is None else scale, name)
 
 
+def poison_unused_mla_slots(x: MlaDecodeInputs, value: float = float("nan")) -> None:
+    """Fill the slots past each sequence's end on its last page, and every page
+    no sequence references, with ``value``."""
+    used = torch.zeros(x.kv_pages.shape[0], dtype=torch.bool)
+    for b in range(x.B):
+        L = int(x.seq_lens[b])
+        n = -(-L // x.page_size)
+        for p in range(n):
+            used[int(x.block_table[b, p])] = True
+        if n and L % x.page_size:
+            x.kv_pages[int(x.block_table[b, n - 1]), L % x.page_size:] = value
+    x.kv_pages[~used] = value
+
+
 def poison_unused_slots(x: DecodeInputs, value: float = float("nan")) -> None:
     """Fill the slots past each sequence's end on its last page with ``value``
     (and any pool page no sequence references). A correct kernel never lets
@@ -364,6 +378,6 @@ def workload_6() -> ChunkInputs:
 
 
 def workload_7() -> MlaDecodeInputs:
-    return mla_decode_inputs(4, 128, 512, 64, (16384, 32768), seed=49,
-                             name="MLA-absorbed decode bf16 B=4 Hq=128 d_c=512 d_r=64 "
-                                  "seq_lens~U[16384,32768] page=16 permuted")
+    return mla_decode_inputs(16, 128, 512, 64, (8192, 16384), seed=49,
+                             name="MLA-absorbed decode bf16 B=16 Hq=128 d_c=512 d_r=64 "
+                                  "seq_lens~U[8192,16384] page=16 permuted")

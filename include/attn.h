@@ -10,6 +10,8 @@
  *       fixed-size pages addressed through a block table, split along the
  *       context and merged by log-sum-exp.
  *   attn_backward : the gradients of the prefill with respect to q, k and v.
+ *   attn_decode_mla : decode for multi-head latent attention with absorbed
+ *       projections (one shared 576-wide latent row per token).
  *   attn_prefill_paged : a chunk of new queries per sequence against the same
  *       paged cache, each row seeing every key up to its own position (the
  *       attention half of chunked prefill); attn_kv_append writes the chunk's
@@ -317,6 +319,41 @@ int attn_backward(const void* q, const void* k, const void* v, const void* o, co
                   const float* lse, void* dq, void* dk, void* dv, int B, int N, int Hq, int Hkv, int d,
                   float scale, int causal, int layout, void* workspace, size_t workspace_bytes,
                   void* stream);
+
+/*
+ * attn_decode_mla_num_splits / attn_decode_mla_workspace_size - split count
+ * (clamped to [1, min(max_pages_per_seq, 1024)]; 0 = automatic, a function of
+ * the arguments only) and fp32 scratch bytes, B*Hq*splits*(512 + 2)*4, of
+ * attn_decode_mla. The workspace size is 0 for invalid sizes.
+ */
+int attn_decode_mla_num_splits(int B, int Hq, int max_pages_per_seq, int num_splits);
+size_t attn_decode_mla_workspace_size(int B, int Hq, int max_pages_per_seq, int num_splits);
+
+/*
+ * attn_decode_mla - one decode step of multi-head latent attention with the
+ * up-projections absorbed ("inference-attention", section "DeepSeek
+ * Multi-head Latent Attention"): each cached token is one row
+ * [c_t ; k^R_t] = [latent (d_c = 512) ; rotary key (d_r = 64)] shared by all
+ * query heads, i.e. multi-query attention with d_k = 576 and d_v = 512 whose
+ * values are the latent columns of the same rows. bf16 in and out.
+ *
+ * q:          [B, Hq, 576] bf16, head h's absorbed query [W_UK,h^T q^C_h ; q^R_h].
+ * kv_pages:   [num_pages, page_size, 576] bf16, the page pool of latent rows [PAGED].
+ * block_table, seq_lens: as for attn_decode (the query is the newest token,
+ *             already cached; L = 0 gives zeros).
+ * o:          [B, Hq, 512] bf16 (out): sum_t softmax_t(scale * q_h . row_t) row_t[0:512]
+ *             (W_UV is applied by the caller).
+ * scale:      the score scale of the heads the latent stands for, usually
+ *             1/sqrt(d_head + d_r).
+ * Requires d_c == 512, d_r == 64, Hq a multiple of 16, page_size == 16 and
+ * workspace_bytes >= attn_decode_mla_workspace_size(...). Preconditions on
+ * device data as for attn_decode. The split boundaries depend only on L and
+ * the split count, so a permuted table gives bit-identical output.
+ */
+int attn_decode_mla(const void* q, const void* kv_pages, const int32_t* block_table, const int32_t* seq_lens,
+                    void* o, int B, int Hq, int d_c, int d_r, int page_size, int max_pages_per_seq,
+                    int num_pages, float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                    void* stream);
 
 /*
  * attn_gather_pages - materialise the logical cache of each sequence from the

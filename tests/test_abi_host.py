@@ -32,7 +32,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) == 13
+    assert len(names) == 16
     for n in names:
         assert hasattr(L, n), n
     assert sorted(n for n, _, _ in binding.SIGNATURES) == names
@@ -213,6 +213,34 @@ def test_backward_workspace_size(L):
     assert L.attn_backward_workspace_size(2, 100, 8) == 2 * 2 * 8 * 128 * 4
     assert L.attn_backward_workspace_size(1, 64, 1) == 2 * 64 * 4
     assert L.attn_backward_workspace_size(0, 64, 1) == 0
+
+
+def mla(L, **kw):
+    a = dict(q=A, kv=A, table=A, lens=A, o=A, B=2, Hq=32, d_c=512, d_r=64, page_size=16, mpps=8, num_pages=16,
+             scale=0.07, splits=0, ws=A, ws_bytes=1 << 30)
+    a.update(kw)
+    return L.attn_decode_mla(a["q"], a["kv"], a["table"], a["lens"], a["o"], a["B"], a["Hq"], a["d_c"], a["d_r"],
+                             a["page_size"], a["mpps"], a["num_pages"], a["scale"], a["splits"], a["ws"],
+                             a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,err", [
+    (dict(kv=None), "ATTN_ERR_NULL"), (dict(table=None), "ATTN_ERR_NULL"), (dict(B=0), "ATTN_ERR_SHAPE"),
+    (dict(Hq=24), "ATTN_ERR_SHAPE"), (dict(d_c=256), "ATTN_ERR_HEAD_DIM"), (dict(d_r=32), "ATTN_ERR_HEAD_DIM"),
+    (dict(page_size=64), "ATTN_ERR_PAGE"), (dict(scale=float("inf")), "ATTN_ERR_SHAPE"),
+    (dict(ws_bytes=100), "ATTN_ERR_WORKSPACE"), (dict(o=A + 2), "ATTN_ERR_ALIGN"), (dict(splits=-1), "ATTN_ERR_SHAPE"),
+])
+def test_decode_mla_rejects(L, kw, err):
+    assert mla(L, **kw) == ERR[err]
+
+
+def test_decode_mla_sizes(L):
+    assert L.attn_decode_mla_num_splits(4, 128, 100, 7) == 7
+    assert L.attn_decode_mla_num_splits(4, 128, 5, 7) == 5
+    auto = L.attn_decode_mla_num_splits(16, 128, 1024, 0)
+    assert 1 <= auto <= 1024 // 64
+    assert L.attn_decode_mla_workspace_size(16, 128, 1024, 0) == 16 * 128 * auto * 514 * 4
+    assert L.attn_decode_mla_workspace_size(16, 120, 1024, 0) == 0
 
 
 def test_binding_refuses_cpu_tensors():
