@@ -276,7 +276,8 @@ def backward_report(dev, stream, steps: int) -> dict:
             "avg_call_us": round(t, 2), "flops_per_call": fl,
             "kernels": "bwd_pre_kernel<128> + bwd_dkdv_kernel<128,4,64> + bwd_dq_kernel<128,8,64>",
             "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / BF16_PEAK_TFLOPS, 4)}}
+                         "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                         "traffic": measured_traffic("backward", BACKWARD_SOURCES)}}
 
 
 def mla_setup(dev, stream):
@@ -308,19 +309,23 @@ def mla_report(dev, stream, steps: int) -> dict:
             "tflops": round(fl / (t * 1e-6) / 1e12, 3),
             "kernels": "mla_split_kernel + mla_merge_kernel",
             "roofline": {"bound": "hbm", "achieved": round(gb, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gb / HBM_PEAK_GBS, 4)}}
+                         "frac": round(gb / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("decode_mla", MLA_SOURCES)}}
 
 
-PREFILL_SOURCES = ["prefill_bf16.hip", "attn_internal.h"]
+PREFILL_SOURCES = ["prefill_bf16.hip", "attn_internal.h", "cdna4.h"]
 DECODE_SOURCES = ["decode.hip", "attn_internal.h"]
 APPEND_SOURCES = ["kv_append.hip", "attn_internal.h"]
+BACKWARD_SOURCES = ["backward_bf16.hip", "attn_internal.h", "cdna4.h"]
+MLA_SOURCES = ["decode_mla.hip", "attn_internal.h", "cdna4.h"]
 
 
 def write_traffic(root: str) -> int:
     """Turn rocprofv3 --pmc CSVs into profiles/traffic.json (no GPU needed).
 
     Expects <root>/<COUNTER>_<kind>/**/*counter_collection.csv for COUNTER in
-    FETCH_SIZE, WRITE_SIZE and kind in prefill, decode, chunked, append, copy,
+    FETCH_SIZE, WRITE_SIZE and kind in prefill, decode, chunked, append,
+    backward, mla, copy,
     as written by
         rocprofv3 --pmc <COUNTER> -d <root>/<COUNTER>_<kind> -o run --output-format csv \
             -- python bench.py --only <kind> --steps 3 --warmup 1 > <root>/<COUNTER>_<kind>.log
@@ -351,7 +356,10 @@ def write_traffic(root: str) -> int:
                                    ("decode", "decode", ["decode_split_kernel", "decode_merge_kernel"],
                                     DECODE_SOURCES),
                                    ("prefill_paged", "chunked", ["prefill_bf16_kernel"], PREFILL_SOURCES),
-                                   ("kv_append", "append", ["kv_append_kernel"], APPEND_SOURCES)]:
+                                   ("kv_append", "append", ["kv_append_kernel"], APPEND_SOURCES),
+                                   ("backward", "backward", ["bwd_pre_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"],
+                                    BACKWARD_SOURCES),
+                                   ("decode_mla", "mla", ["mla_split_kernel", "mla_merge_kernel"], MLA_SOURCES)]:
         for counter in ("FETCH_SIZE", "WRITE_SIZE"):
             ran = None
             with open(os.path.join(root, f"{counter}_{kind}.log")) as f:
@@ -418,8 +426,7 @@ def only(args, dev) -> int:
     b.record(stream)
     torch.cuda.synchronize()
     srcs = {"prefill": PREFILL_SOURCES, "decode": DECODE_SOURCES, "chunked": PREFILL_SOURCES,
-            "append": APPEND_SOURCES, "backward": ["backward_bf16.hip", "attn_internal.h", "cdna4.h"],
-            "mla": ["decode_mla.hip", "attn_internal.h", "cdna4.h"]}.get(args.only)
+            "append": APPEND_SOURCES, "backward": BACKWARD_SOURCES, "mla": MLA_SOURCES}.get(args.only)
     print(json.dumps({"only": args.only, "steps": args.steps,
                       "avg_us": round(a.elapsed_time(b) * 1e3 / args.steps, 2),
                       "source_sha256": source_hash(*srcs) if srcs else None, **work}), flush=True)
