@@ -30,9 +30,16 @@ FLAGS = [
 ]
 
 
+# Per-source flags. The dK/dV kernel needs more than the 256 architectural
+# VGPRs; with MFMA results in VGPRs the overflow goes to a few AGPRs instead
+# of the gradient accumulators being copied to and from AGPRs around every
+# product (measured 10% faster backward).
+EXTRA = {"backward_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

@@ -23,6 +23,8 @@
 // products. Score tiles are held in the MFMA accumulator layout whose lanes
 // already form the B operand of the next product (the key/query order of each
 // 16-wide k-step is the accumulator's), as in the forward.
+#include <type_traits>
+
 #include "attn_internal.h"
 #include "cdna4.h"
 
@@ -243,34 +245,42 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams p, int n
         sc = mfma_32x32x16(a, kreg[s], sc);
         dp = mfma_32x32x16(d, vreg[s], dp);
       }
-      // P = 2^(S c2 - lse2), dS = P (dP - D); both packed as B operands
+      // P = 2^(S c2 - lse2), dS = P (dP - D); both packed as B operands. The
+      // mask is applied only on the tiles that need it (a uniform choice) and
+      // with bit operations, so no lane-divergent branch enters the loop.
       u32x4_t pp[2], ds[2];
+      auto make_p = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row4 = rb * 32 + 8 * r + 4 * h2;  // first of this lane's 4 rows in group r
-        const f32x4_t l2 = *(const f32x4_t*)(st + row4 * 4);
-        const f32x4_t dd = *(const f32x4_t*)(st + 256 + row4 * 4);
-        float pv[4], dsv[4];
+        for (int r = 0; r < 4; ++r) {
+          const int row4 = rb * 32 + 8 * r + 4 * h2;  // first of this lane's 4 rows in group r
+          const f32x4_t l2 = *(const f32x4_t*)(st + row4 * 4);
+          const f32x4_t dd = *(const f32x4_t*)(st + 256 + row4 * 4);
+          float pv[4], dsv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = 4 * r + i;
-          float pe = __builtin_amdgcn_exp2f(fmaf(sc[e], c2, -l2[i]));
-          if (need_mask) {
-            const int qrow = r0 + row4 + i;
-            const bool vis = qrow < N && kj < N && (!p.causal || kj <= qrow);
-            pe = vis ? pe : 0.f;
+          for (int i = 0; i < 4; ++i) {
+            const int e = 4 * r + i;
+            float pe = __builtin_amdgcn_exp2f(fmaf(sc[e], c2, -l2[i]));
+            if constexpr (decltype(masked)::value) {
+              const int qrow = r0 + row4 + i;
+              const unsigned vis = (unsigned)(qrow < N) & (unsigned)(kj < N) & (unsigned)(!p.causal | (kj <= qrow));
+              pe = __uint_as_float(__float_as_uint(pe) & (0u - vis));
+            }
+            pv[i] = pe;
+            dsv[i] = pe * (dp[e] - dd[i]);
           }
-          pv[i] = pe;
-          dsv[i] = pe * (dp[e] - dd[i]);
+          // k-step ps = 2 rb + r/2 holds rows (r even: e 0-7 -> elements 0..3 of
+          // the pack, r odd: 4..7); words 2(r&1), 2(r&1)+1
+          const int kk = r >> 1, wd = (r & 1) * 2;
+          pp[kk][wd] = pack_bf16x2(pv[0], pv[1]);
+          pp[kk][wd + 1] = pack_bf16x2(pv[2], pv[3]);
+          ds[kk][wd] = pack_bf16x2(dsv[0], dsv[1]);
+          ds[kk][wd + 1] = pack_bf16x2(dsv[2], dsv[3]);
         }
-        // k-step ps = 2 rb + r/2 holds rows (r even: e 0-7 -> elements 0..3 of
-        // the pack, r odd: 4..7); words 2(r&1), 2(r&1)+1
-        const int kk = r >> 1, wd = (r & 1) * 2;
-        pp[kk][wd] = pack_bf16x2(pv[0], pv[1]);
-        pp[kk][wd + 1] = pack_bf16x2(pv[2], pv[3]);
-        ds[kk][wd] = pack_bf16x2(dsv[0], dsv[1]);
-        ds[kk][wd + 1] = pack_bf16x2(dsv[2], dsv[3]);
-      }
+      };
+      if (need_mask)
+        make_p(std::true_type{});
+      else
+        make_p(std::false_type{});
       // dV^T += dO^T P and dK^T += Q^T dS (rows d, columns this wave's keys)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -468,22 +478,28 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p, int n_q
         dp = mfma_32x32x16(v, doreg[s], dp);
       }
       u32x4_t ds[2];
+      auto make_ds = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-      for (int e2 = 0; e2 < 8; ++e2) {
-        float dsv[2];
+        for (int e2 = 0; e2 < 8; ++e2) {
+          float dsv[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int e = 2 * e2 + i;
-          float pe = __builtin_amdgcn_exp2f(fmaf(sc[e], c2, -l2));
-          if (need_mask) {
-            const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * h2 + (e & 3);
-            const bool vis = key < N && qi < N && (!p.causal || key <= qi);
-            pe = vis ? pe : 0.f;
+          for (int i = 0; i < 2; ++i) {
+            const int e = 2 * e2 + i;
+            float pe = __builtin_amdgcn_exp2f(fmaf(sc[e], c2, -l2));
+            if constexpr (decltype(masked)::value) {
+              const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * h2 + (e & 3);
+              const unsigned vis = (unsigned)(key < N) & (unsigned)(qi < N) & (unsigned)(!p.causal | (key <= qi));
+              pe = __uint_as_float(__float_as_uint(pe) & (0u - vis));
+            }
+            dsv[i] = pe * (dp[e] - dd);
           }
-          dsv[i] = pe * (dp[e] - dd);
+          ds[e2 >> 2][e2 & 3] = pack_bf16x2(dsv[0], dsv[1]);
         }
-        ds[e2 >> 2][e2 & 3] = pack_bf16x2(dsv[0], dsv[1]);
-      }
+      };
+      if (need_mask)
+        make_ds(std::true_type{});
+      else
+        make_ds(std::false_type{});
       // dQ^T += K^T dS^T
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
