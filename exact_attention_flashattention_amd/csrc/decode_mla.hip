@@ -12,9 +12,11 @@
 //
 // Mapping onto CDNA4: a work-group of 8 waves takes one (sequence, split,
 // 128-head chunk); wave w owns 16 heads. Each step stages two pages (32
-// tokens, 36 KiB) into LDS with global_load_lds, rows padded to 1168 bytes so
-// that both the row reads and the transposed reads below are free of bank
-// conflicts; a ring of four step buffers keeps three steps of loads in flight.
+// tokens, 36 KiB) into LDS with global_load_lds, rows padded to 1184 bytes
+// (of the strides 1152..1280 with and without XOR swizzles of the 16-byte
+// chunks, the one under which the row reads below ran fastest: ~140 B/clk
+// per CU against 126 at 1168 and 64 unpadded); a ring of four step buffers
+// keeps three steps of loads in flight.
 //  * S^T (32 tokens x 16 heads) = K q^T with v_mfma_f32_16x16x32_bf16, A = K
 //    rows from LDS, B = the wave's 16 queries (576 dims) held in registers.
 //  * Online softmax per head (lane column), with the lazy rescale used by the
@@ -42,10 +44,10 @@ constexpr int PG = 16;                   // tokens per page
 constexpr int NWM = 8;                   // waves per work-group (16 heads each)
 constexpr int HPW = 16;                  // heads per wave
 constexpr int ROWG = DK * 2;             // bytes of a cached row in HBM (1152)
-constexpr int ROWP = ROWG + 16;          // bytes of a row in LDS (padded)
-constexpr int SLOTS_ROW = ROWP / 16;     // 16-byte slots per LDS row (73)
+constexpr int ROWP = ROWG + 32;          // bytes of a row in LDS (padded)
+constexpr int SLOTS_ROW = ROWP / 16;     // 16-byte slots per LDS row (74)
 constexpr int STEP_ROWS = 2 * PG;        // tokens per step
-constexpr int STEP_SLOTS = STEP_ROWS * SLOTS_ROW;        // 2336
+constexpr int STEP_SLOTS = STEP_ROWS * SLOTS_ROW;        // 2368
 constexpr int IPW_M = (STEP_SLOTS + 64 * NWM - 1) / (64 * NWM);  // load instructions per wave (5)
 constexpr int STEP_BYTES = IPW_M * NWM * 1024;           // one ring buffer (40 KiB)
 constexpr int NBUF_M = 4;
@@ -99,8 +101,8 @@ __global__ __launch_bounds__(NWM * 64, 1) void mla_split_kernel(MlaParams p, int
   for (int vb = 0; vb < VB; ++vb) oacc[vb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_ref = kNegInf, l_run = 0.f;
 
-  // ---- staging: slot s of a step buffer holds row s / 73, chunk s % 73 ---------
-  // (chunk 72 is the row's padding; slots past the 32 rows are spare). A row
+  // ---- staging: slot s of a step buffer holds row s / 74, chunk s % 74 ---------
+  // (chunks 72 and 73 are the row's padding; slots past the 32 rows are spare). A row
   // past the end of the sequence, or the missing second page of the last
   // step, is loaded from the sequence's last token.
   auto issue = [&](int step) __attribute__((always_inline)) {
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(NWM * 64, 1) void mla_split_kernel(MlaParams p, int
       if (s >= STEP_SLOTS) s = 0;  // spare slot: a harmless copy of slot 0's source
       const int row = s / SLOTS_ROW;
       int chunk = s - row * SLOTS_ROW;
-      if (chunk == SLOTS_ROW - 1) chunk = SLOTS_ROW - 2;  // padding: any chunk of the row
+      if (chunk >= ROWG / 16) chunk = ROWG / 16 - 1;  // padding: any chunk of the row
       const int lp = row < PG ? pa : pb;                   // logical page of the row
       int t = lp * PG + (row & (PG - 1));
       int page = row < PG ? page_a : page_b;
