@@ -102,11 +102,24 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   const int per_pair = n_qtiles * g;
   // (kv head, b) pairs with b fastest: an XCD's contiguous range then holds
   // the same KV heads of different sequences, which keeps the XCDs balanced
-  // when the sequences differ in length
-  const int pair = w / per_pair;
-  const int rem = w - pair * per_pair;
-  const int qtile = n_qtiles - 1 - rem / g; // heaviest causal tiles first
-  const int hg = rem - (rem / g) * g;
+  // when the sequences differ in length. Inside a group of G pairs the
+  // heaviest causal query tiles of all G pairs come first (longest work
+  // first). A pair with at least as many work items as an XCD has CUs keeps
+  // G = 1; a smaller one (few query tiles, few query heads per KV head) would
+  // leave its light tiles to run beside the next pair's heavy ones, so its
+  // group is an XCD's whole share of pairs (measured: MHA at d = 64, N = 2048
+  // 141 -> 95 us; larger pairs lose a little L2 locality when grouped).
+  constexpr int kCusPerXcd = 32;
+  const int n_pairs = p.B * p.Hkv;
+  const int G = per_pair >= kCusPerXcd ? 1 : max(1, min(n_pairs, (total >> 3) / per_pair));
+  const int grp = w / (G * per_pair);
+  const int r_in = w - grp * G * per_pair;
+  const int row_items = min(G, n_pairs - grp * G) * g;  // items per query-tile rank in this group
+  const int qrank = r_in / row_items;
+  const int rest = r_in - qrank * row_items;
+  const int pair = grp * G + rest / g;
+  const int qtile = n_qtiles - 1 - qrank;  // heaviest causal tiles first
+  const int hg = rest - (rest / g) * g;
   const int kvh = pair / p.B;
   const int b = pair - kvh * p.B;
   const int h = kvh * g + hg;
