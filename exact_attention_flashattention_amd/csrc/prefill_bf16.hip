@@ -29,23 +29,24 @@
 //    stored at a position XOR-swizzled by the row, chosen so that both the K
 //    operand reads (16 consecutive rows, one chunk each) and the transposed V
 //    reads (4 consecutive rows, two chunks each) hit distinct LDS banks.
-//  * Software pipeline: while tile j's scores are exponentiated and multiplied
-//    into V (vector ALU + MFMA), the MFMAs of tile j+1's scores are already in
-//    flight, all in one basic block, so the matrix cores and the vector ALU
-//    work at the same time. Four LDS buffers rotate: tile j (V read), tile
-//    j+1 (K read), tile j+2 (landed) and tile j+3 (loads in flight, issued
-//    three iterations before use); one barrier per tile.
+//  * Software pipeline: iteration j first issues the MFMAs of tile j+1's
+//    scores, then takes tile j's row max (those scores finished an iteration
+//    earlier, so nothing waits on an MFMA result), then exponentiates tile j
+//    with its P.V MFMAs interleaved. Four LDS buffers rotate: tile j (V
+//    read), tile j+1 (K read), tile j+2 (landed) and tile j+3 (loads in
+//    flight, issued three iterations before use); one barrier per tile.
 //  * The reference point m used in 2^(s - m) is only moved when a row's max
-//    exceeds it by more than 2^8 (then O and l are rescaled exactly); between
-//    moves the weights are bounded by 2^8, which bf16 and fp32 represent with
-//    the same relative precision. Results are identical in exact arithmetic;
-//    the decision for tile j+1 is taken after tile j's P.V, outside the
-//    pipelined block, so the accumulators are untouched on most tiles.
+//    exceeds it by more than 2^8 (a wave-uniform ballot; then O and l are
+//    rescaled exactly); between moves the weights are bounded by 2^8, which
+//    bf16 and fp32 represent with the same relative precision. Results are
+//    identical in exact arithmetic, and the accumulators are untouched on
+//    most tiles.
 //  * Row sums of P are taken from the bf16-rounded weights (dot2 against
 //    ones), so numerator and denominator use the same weights.
 //  * Work-groups are numbered so that each XCD receives whole (b, KV head)
-//    groups (its L2 then holds those K/V), and within a group the heaviest
-//    causal query tiles start first.
+//    pairs (its L2 then holds those K/V), and the heaviest causal query tiles
+//    start first: within a pair, or across all of an XCD's pairs when a pair
+//    has fewer work items than the XCD has CUs.
 //  * Inputs must be finite: rows past the end of the sequence are filled with
 //    the last row (finite) and masked out of the softmax, so their weight is
 //    exactly 0.
@@ -539,7 +540,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   for (int i = 0; i < 32 / RPI; ++i) {
     const int r = i * RPI + lane / CPR, ch = lane % CPR;
     const u32x4_t val = *(const u32x4_t*)(ost + r * OROW + ch * 16);
-    if (qw0 + r < Nq) *(u32x4_t*)(og + (long long)(qw0 + r) * p.o_sn + ch * 8) = val;
+    // non-temporal: O is written once and not read here, so its lines go out
+    // to HBM while this compute-bound kernel runs instead of lingering dirty
+    // in the caches until a later, bandwidth-bound kernel evicts them
+    if (qw0 + r < Nq) __builtin_nontemporal_store(val, (u32x4_t*)(og + (long long)(qw0 + r) * p.o_sn + ch * 8));
   }
   // m_ref is in units of scale * log2(e) * q.k (the sign fold leaves that product unchanged)
   if (p.lse && h2 == 0 && qi < Nq)
