@@ -59,9 +59,16 @@ __device__ __forceinline__ int swz(int r) {
     return ((r & 3) << 1) | ((r >> 2) & 1);
 }
 
+// cache-policy bit of a non-temporal access (the SLC position on CDNA3/4)
+constexpr int kCachePolicyNT = 2;
 __device__ __forceinline__ void load_to_lds(const void* g, unsigned char* l) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
                                    (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+// the same copy with the non-temporal cache policy, for data read once
+__device__ __forceinline__ void load_to_lds_stream(const void* g, unsigned char* l) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)l, 16, 0, kCachePolicyNT);
 }
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding)

@@ -31,6 +31,9 @@
 //    O^T (d x heads) += V^T P^T with v_mfma_f32_16x16x16_bf16; slots past the
 //    end of the sequence are written as zeros so that a NaN left in an unused
 //    slot cannot reach the output (0 * NaN would).
+//  * K and V are read with non-temporal loads: every cached byte is read once
+//    per call, so it should not displace what other kernels keep in the
+//    caches (measured: 330 -> 313 us for the long-context decode).
 //  * Each wave keeps ATTN_DECODE_PREFETCH pages of loads in flight ahead of
 //    the page it consumes, and caches its next 64 block-table entries in one
 //    register (lane t holds entry t), so no load waits on a table lookup.
@@ -176,12 +179,12 @@ __global__ __launch_bounds__(NWU * 64, ATTN_DECODE_WAVES_PER_SIMD) void decode_s
     const int phys = phys_of(pg);
 #pragma unroll
     for (int s = 0; s < C::KS; ++s)
-      kr[s] = *(const u32x4_t*)(kp + kv_row_offset(phys, j, kvh, p.Hkv, D) + s * 32 + rg * 8);
+      kr[s] = __builtin_nontemporal_load((const u32x4_t*)(kp + kv_row_offset(phys, j, kvh, p.Hkv, D) + s * 32 + rg * 8));
 #pragma unroll
     for (int i = 0; i < C::VCH; ++i) {
       const int ch = lane + 64 * i;
       const int slot = ch / (D / 8), dch = ch - slot * (D / 8);
-      vr[i] = *(const u32x4_t*)(vp + kv_row_offset(phys, slot, kvh, p.Hkv, D) + dch * 8);
+      vr[i] = __builtin_nontemporal_load((const u32x4_t*)(vp + kv_row_offset(phys, slot, kvh, p.Hkv, D) + dch * 8));
     }
   };
 

@@ -128,7 +128,7 @@ __global__ __launch_bounds__(NWM * 64, 1) void mla_split_kernel(MlaParams p, int
         page = page_last;
       }
       const unsigned char* src = pool + ((long long)page * PG + (t & (PG - 1))) * ROWG + chunk * 16;
-      load_to_lds(src, buf + i * 1024);
+      load_to_lds_stream(src, buf + i * 1024);  // each latent row is read once per call
     }
   };
 
