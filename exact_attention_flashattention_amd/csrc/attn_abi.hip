@@ -141,7 +141,15 @@ int attn_decode_ex(const void* q, const void* k_pages, const void* v_pages,
   if ((long long)max_pages_per_seq * page_size > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   if ((long long)num_pages * page_size * Hkv * d > kMaxElems) return ATTN_ERR_SHAPE;
   if ((long long)B * max_pages_per_seq > kMaxElems) return ATTN_ERR_SHAPE;
-  const int S = attn_decode_num_splits(B, Hkv, max_pages_per_seq, num_splits);
+  // with a window the automatic split count is taken over the pages a query
+  // can see (never more than without it, so the workspace size still fits)
+  int split_pages = max_pages_per_seq;
+  if (variant && variant->window > 0) {
+    const long long vis = ((long long)variant->window + 15) / 16 + 1 + ((long long)variant->n_sink + 15) / 16;
+    if (vis < split_pages) split_pages = (int)vis;
+  }
+  const int S = num_splits > 0 ? attn_decode_num_splits(B, Hkv, max_pages_per_seq, num_splits)
+                               : attn_decode_num_splits(B, Hkv, split_pages, 0);
   const size_t need = attn_decode_workspace_size(B, Hq, Hkv, d, max_pages_per_seq, num_splits);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o) ||

@@ -394,10 +394,17 @@ hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
 }  // namespace
 
 int auto_decode_splits(int B, int Hkv, int max_pages_per_seq) {
-  // aim for about 4096 (sequence, KV head, split) waves, at least 16 pages each
-  const long long pairs = (long long)B * Hkv;
-  long long s = (4096 + pairs - 1) / pairs;
-  const long long cap = max(1, max_pages_per_seq / 16);
+  // One round of work-groups: B * ceil(Hkv / 8) * S work-groups of 8 waves
+  // close to (not above) 256, the compute units of an MI355X, each split
+  // holding at least 4 pages. Measured on the long-context and batched decode
+  // workloads and on the 8192-token window: a round of exactly the CU count
+  // beats two rounds, and counts that leave CUs with one work-group more than
+  // others run up to 30% slower. A constant, not a device query, keeps the
+  // choice (and so the summation order) a function of the arguments only.
+  constexpr long long kTargetWorkGroups = 256;
+  const long long wgs = (long long)B * ((Hkv + NWU - 1) / NWU);
+  long long s = kTargetWorkGroups / wgs;
+  const long long cap = max(1, max_pages_per_seq / 4);
   if (s > cap) s = cap;
   if (s < 1) s = 1;
   return (int)s;

@@ -280,7 +280,10 @@ int attn_prefill_paged(const void* q, const void* k_pages, const void* v_pages,
  * t >= L - W and t < n_sink, and only the pages holding them are read (the
  * splits cut those pages); a sink logit joins the merge as one more partial
  * with max s_h, sum 1 and zero output [SDPA] section 10. The workspace size
- * and split count are those of attn_decode for the same arguments.
+ * is that of attn_decode for the same arguments; with num_splits = 0 and a
+ * window, the automatic split count is attn_decode_num_splits taken with
+ * max_pages_per_seq replaced by the pages a window can touch,
+ * min(max_pages_per_seq, ceil(W/16) + 1 + ceil(n_sink/16)) (page_size 16).
  */
 int attn_decode_ex(const void* q, const void* k_pages, const void* v_pages,
                    const int32_t* block_table, const int32_t* seq_lens, void* o,
