@@ -82,6 +82,10 @@ BF16_CASES = [
     (2, 257, 8, 2, 128),   # one past a query tile
     (1, 333, 6, 3, 64),    # ragged, several tiles
     (1, 600, 4, 2, 128),   # several query tiles, ragged tail
+    # MHA with few query tiles per (b, KV head) pair: the pairs are grouped
+    # (4 per group here) with a partial last group of 3
+    (7, 512, 5, 5, 64),
+    (5, 600, 7, 7, 128),
 ]
 
 
