@@ -139,7 +139,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams p, int n
 #pragma unroll
     for (int e = 0; e < 16; ++e) dk[db][e] = dv[db][e] = 0.f;
 
-  // streamed slots: (query head hg, query tile t0 + r)
+  // streamed slots: (query head hg, query tile T - 1 - r). The tiles of a
+  // head run from the last one down to the block's first: the work-groups of
+  // one (b, KV head) run side by side, and all of them start on the same last
+  // tile, so they read the same Q/dO tiles at about the same time and L2
+  // serves most of them (HBM reads of this kernel 1.67 GB -> 0.75 GB on the
+  // headline backward; ascending order had each group start on its own tile).
   const int T = (N + BN - 1) / BN;
   const int t0 = p.causal ? k_blk0 / BN : 0;
   const int nT = T - t0;
@@ -161,7 +166,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams p, int n
   }
   constexpr int kLoads = 2 * C::IPW + 1;  // Q and dO pieces, plus the stats copy
   auto issue = [&](int slot) __attribute__((always_inline)) {
-    const int hg = slot / nT, t = t0 + (slot - hg * nT);
+    const int hg = slot / nT, t = T - 1 - (slot - hg * nT);
     const int h = kvh * g + hg;
     const int r0 = t * BN;
     const char* qt = (const char*)((const __bf16*)p.q + b * p.q_sb + h * p.q_sh) + (long long)r0 * row_bytes;
@@ -225,7 +230,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams p, int n
 
   // one streamed slot: the query tile's contribution to this wave's dK, dV
   auto compute = [&](int slot) __attribute__((always_inline)) {
-    const int hg = slot / nT, t = t0 + (slot - hg * nT);
+    const int hg = slot / nT, t = T - 1 - (slot - hg * nT);
     const int r0 = t * BN;
     const unsigned char* qt = qbuf(slot);
     const unsigned char* dt = dbuf(slot);
@@ -304,7 +309,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams p, int n
   for (int j = 0; j < n_slots; ++j) {
     if (j + 3 < n_slots) issue(j + 3);
     const int r = j % nT;
-    if (wave_live && r >= w_t0) compute(j);
+    if (wave_live && r <= nT - 1 - w_t0) compute(j);
     wait_tiles_after(min(n_slots - j - 2, 2));
     __syncthreads();
   }
