@@ -211,14 +211,28 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   const int n_slots = sink_tiles + max(n_tiles - win_lo, 0);
   auto tile_of = [&](int j) __attribute__((always_inline)) { return j < sink_tiles ? j : win_lo + (j - sink_tiles); };
   auto slot_of = [&](int t) __attribute__((always_inline)) { return t < sink_tiles ? t : t - win_lo + sink_tiles; };
-  // slots w_first .. w_end-1 hold keys visible to some row of this wave (with
-  // initial-token tiles, the slots between them and the wave's window are
-  // included and fully masked)
+  // Slots w_first .. w_end-1 hold keys visible to some row of this wave. With
+  // initial-token tiles the wave also visits the sink slots 0 .. sink_tiles-1
+  // first; when its own window starts past them (sink_gap) the slots in
+  // between are skipped like those of a later wave.
   int w_first = 0, w_end = 0;
+  bool sink_gap = false;
   if (qw0 < Nq) {
     const int last = (p.causal ? min(n_tiles, (P + qw0 + 31) / BN + 1) : n_tiles) - 1;
     w_end = slot_of(last) + 1;
-    if (W > 0 && sink_tiles == 0) w_first = slot_of(max(P + qw0 - W + 1, 0) / BN);
+    if (W > 0) {
+      const int t_w = max(P + qw0 - W + 1, 0) / BN;  // the wave's first window tile
+      if (sink_tiles == 0) {
+        w_first = slot_of(t_w);
+      } else {
+        // t_w >= sink_tiles implies t_w >= win_lo, so slot_of(t_w) is its slot
+        const int ws = t_w >= sink_tiles ? slot_of(t_w) : 0;
+        if (ws > sink_tiles && ws < w_end) {
+          sink_gap = true;
+          w_first = ws;
+        }
+      }
+    }
   }
 
   // ---- HBM -> LDS copies of K/V tiles ----------------------------------------------
@@ -437,7 +451,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
     wait_vmcnt<0>();
   }
   __syncthreads();
-  if (w_first == 0 && w_end > 0) qk(kbuf(0), sa);
+  if ((w_first == 0 || sink_gap) && w_end > 0) qk(kbuf(0), sa);
 
   // ---- main loop: iteration j consumes slot j and computes the scores of j+1 -------
   // Every wave runs n_slots iterations (one barrier each); the loops only
@@ -488,6 +502,12 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
     end_iteration(j);
   };
   int j = 0;
+  if (sink_gap) {  // the sink slots, then a gap up to the wave's window
+    for (; j + 1 < sink_tiles; ++j) single_step(j);
+    last_step(j, kbuf(j + 3), vbuf(j));
+    end_iteration(j);
+    ++j;
+  }
   for (; j + 1 < w_first; ++j) idle_step(j);
   if (w_first > 0 && w_first < w_end) {
     first_step(j, kbuf(j + 3), kbuf(j + 1));
