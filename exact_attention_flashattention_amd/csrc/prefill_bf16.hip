@@ -384,12 +384,14 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
           s[kb][e] = (off > lim || (off < lo && off >= sk)) ? kNegInf : s[kb][e];
         }
     }
-    float mr = kNegInf;
+    // row max over four interleaved running maxima (one running max would be
+    // a single chain of dependent v_max3 on the critical path of every tile)
+    float rm[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mr = fmaxf(mr, s[kb][e]);
-    mr = halves_max(mr);
+      for (int e = 0; e < 16; ++e) rm[e & 3] = fmaxf(rm[e & 3], s[kb][e]);
+    const float mr = halves_max(fmaxf(fmaxf(rm[0], rm[1]), fmaxf(rm[2], rm[3])));
     const float mt = (mr == kNegInf) ? kNegInf : mr * c2;
     if (__builtin_amdgcn_ballot_w64(mt > m_ref + kRescaleTau)) {
       const float m_new = fmaxf(m_ref, mt);
