@@ -454,7 +454,7 @@ def main() -> int:
         return write_traffic(args.write_traffic)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(the kernels would shard over (batch, KV head) with no exchange)",
               file=sys.stderr)
         return 2
