@@ -168,3 +168,74 @@ def test_decode_variant_is_the_last_prefill_row():
     e = (dec.cpu().double() - pre[:, N - 1].cpu().double()).abs().max().item()
     log(f"  decode vs prefill last row: {e:.3e}")
     assert e <= 2 * BF16_MAX
+
+
+# ---- the variant workloads bench.py times, at full size, on sampled outputs ----
+
+BENCH_W, BENCH_S = 1024, 4          # prefill: window and initial tokens
+BENCH_WD = 8192                     # decode: window
+
+
+def test_windowed_prefill_full_size_sampled():
+    """Headline prefill shape (B=4 N=4096 Hq=32 Hkv=8 d=128) with a 1024 window,
+    4 initial tokens and per-head sink logits, as timed: sampled rows (the
+    first row, both sides of the window's first full length, the last row and
+    random ones) against the oracle row by row."""
+    x = wl.workload_2()
+    W, S = BENCH_W, BENCH_S
+    sinks = torch.linspace(-1.0, 3.0, x.Hq, dtype=torch.float32)
+    log(f"case: {x.name} window={W} n_sink={S} sinks=linspace(-1, 3)")
+    lse = torch.full((x.B, x.Hq, x.N), float("nan"), device="cuda")
+    o = bd.attn_prefill_ex(x.q.cuda(), x.k.cuda(), x.v.cuda(), scale=x.scale, window=W, n_sink=S,
+                           sinks=sinks.cuda(), lse=lse)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    rng = np.random.default_rng(790)
+    worst = 0.0
+    keys = np.arange(x.N)
+    for b in range(x.B):
+        for i in [0, W - 1, W, W + 1, x.N - 1] + rng.integers(0, x.N, 3).tolist():
+            h = int(rng.integers(0, x.Hq))
+            kv = ao.kv_head_of(h, x.Hq, x.Hkv)
+            allowed = ao.position_mask([i], keys, window=W, n_sink=S)
+            ref, ref_lse = ao.sdpa_masked_ref(x.q[b, i, h][None, None], x.k[b, :, kv][None], x.v[b, :, kv][None],
+                                              x.scale, allowed, sinks=sinks[h:h + 1].numpy())
+            e = np.abs(o[b, i, h].double().numpy() - ref[0, 0]).max()
+            worst = max(worst, e)
+            assert e <= BF16_MAX, (b, i, h, e)
+            assert abs(float(lse[b, h, i]) - ref_lse[0, 0]) <= LSE_BF16, (b, i, h)
+    log(f"  sampled max-abs {worst:.3e}")
+
+
+def test_windowed_decode_full_size_sampled():
+    """Long-context paged decode (B=4 Hq=64 Hkv=8 d=128, 96K-128K tokens,
+    permuted pages) with an 8192 window, 4 initial tokens and per-head sink
+    logits, as timed. The oracle reads only the visible tokens (the anchors
+    and the window), gathered through the block table here."""
+    x = wl.workload_5()
+    W, S = BENCH_WD, BENCH_S
+    sinks = torch.linspace(-1.0, 3.0, x.Hq, dtype=torch.float32)
+    log(f"case: {x.name} window={W} n_sink={S} sinks=linspace(-1, 3)")
+    o = bd.attn_decode_ex(x.q.cuda(), x.k_pages.cuda(), x.v_pages.cuda(), x.block_table.cuda(),
+                          x.seq_lens.cuda(), scale=x.scale, window=W, n_sink=S, sinks=sinks.cuda())
+    torch.cuda.synchronize()
+    o = o.cpu()
+    assert bool(torch.isfinite(o.float()).all())
+    rng = np.random.default_rng(791)
+    worst = 0.0
+    for b in range(x.B):
+        L = int(x.seq_lens[b])
+        pos = np.arange(L)
+        vis = pos[ao.position_mask([L - 1], pos, window=W, n_sink=S)[0]]
+        pages = x.block_table[b].numpy()[vis // x.page_size]
+        slots = vis % x.page_size
+        for h in [0, x.Hq - 1] + rng.integers(0, x.Hq, 4).tolist():
+            kv = ao.kv_head_of(h, x.Hq, x.Hkv)
+            K = x.k_pages[pages, slots, kv].float().numpy()
+            V = x.v_pages[pages, slots, kv].float().numpy()
+            ref, _ = ao.sdpa_masked_ref(x.q[b, h][None, None], K[None], V[None], x.scale,
+                                        np.ones((1, len(vis)), dtype=bool), sinks=sinks[h:h + 1].numpy())
+            e = np.abs(o[b, h].double().numpy() - ref[0, 0]).max()
+            worst = max(worst, e)
+            assert e <= BF16_MAX, (b, h, e)
+    log(f"  sampled max-abs {worst:.3e}")
