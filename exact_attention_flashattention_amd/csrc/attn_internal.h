@@ -110,8 +110,8 @@ hipError_t launch_gather(const void* pages, const int32_t* block_table,
                          int page_size, int max_pages_per_seq, int max_len,
                          int elem_bytes, hipStream_t stream);
 
-// Split count chosen when the caller passes 0: about 4096 (sequence, KV head,
-// split) waves, with at least 16 pages per split.
+// Split count chosen when the caller passes 0: one round of work-groups (about
+// 256 of them, the CU count), with at least 4 pages per split.
 int auto_decode_splits(int B, int Hkv, int max_pages_per_seq);
 
 }  // namespace attn
