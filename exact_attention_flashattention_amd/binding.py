@@ -33,8 +33,9 @@ SIGNATURES = [
     ("attn_prefill_ex", _i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _i, _var, _vp]),
     ("attn_decode_num_splits", _i, [_i, _i, _i, _i]),
     ("attn_decode_workspace_size", _sz, [_i, _i, _i, _i, _i, _i]),
-    ("attn_decode", _i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
-    ("attn_decode_ex", _i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _var, _vp,
+    ("attn_decode", _i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _sz,
+                         _vp]),
+    ("attn_decode_ex", _i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _var, _vp,
                             _sz, _vp]),
     ("attn_kv_append", _i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
     ("attn_prefill_paged", _i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
@@ -92,6 +93,24 @@ def _stream(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
     return getattr(stream, "cuda_stream", stream)
+
+
+def _scratch(nbytes: int, device, stream):
+    """fp32 scratch for one call, allocated on the stream the call's kernels
+    run on. The caching allocator keys a freed block by the stream it was
+    allocated on, so when the tensor is dropped right after the enqueue its
+    memory is only handed to later work on that same stream, which runs after
+    these kernels (a block allocated on another stream could be reused there
+    while the kernels still write it)."""
+    import torch
+    if stream is None:
+        ts = torch.cuda.current_stream(device)
+    elif isinstance(stream, torch.cuda.Stream):
+        ts = stream
+    else:
+        ts = torch.cuda.ExternalStream(int(stream), device=device)
+    with torch.cuda.stream(ts):
+        return torch.empty(max(nbytes, 16) // 4 + 4, dtype=torch.float32, device=device)
 
 
 def _check(status: int, where: str) -> None:
@@ -228,12 +247,12 @@ def _decode(q, k_pages, v_pages, block_table, seq_lens, o, scale, num_splits, wo
         o = torch.empty_like(q)
     need = attn_decode_workspace_size(B, Hq, Hkv, d, mpps, num_splits)
     if workspace is None:
-        workspace = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+        workspace = _scratch(need, q.device, stream)
     ws_bytes = workspace.numel() * workspace.element_size()
     args = (_dev(q, "q"), _dev(k_pages, "k_pages"), _dev(v_pages, "v_pages"),
             _dev(block_table, "block_table"), _dev(seq_lens, "seq_lens"), _dev(o, "o"),
             B, Hq, Hkv, d, page_size, mpps, num_pages, float(d ** -0.5 if scale is None else scale),
-            num_splits)
+            num_splits, ATTN_BF16)
     tail = (_dev(workspace, "workspace"), ws_bytes, _stream(stream))
     if variant is None:
         st = lib().attn_decode(*args, *tail)
@@ -347,7 +366,7 @@ def attn_backward(q, k, v, o, dout, lse, dq=None, dk=None, dv=None, *, causal: b
     dv = torch.empty_like(v) if dv is None else dv
     need = attn_backward_workspace_size(B, N, Hq)
     if workspace is None:
-        workspace = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+        workspace = _scratch(need, q.device, stream)
     st = lib().attn_backward(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _dev(dout, "dout"),
                              _dev(lse, "lse"), _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"), B, N, Hq,
                              Hkv, d, float(d ** -0.5 if scale is None else scale), int(bool(causal)),
@@ -385,7 +404,7 @@ def attn_decode_mla(q, kv_pages, block_table, seq_lens, o=None, *, scale: Option
         o = torch.empty((B, Hq, d_c), dtype=q.dtype, device=q.device)
     need = attn_decode_mla_workspace_size(B, Hq, mpps, num_splits)
     if workspace is None:
-        workspace = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+        workspace = _scratch(need, q.device, stream)
     st = lib().attn_decode_mla(_dev(q, "q"), _dev(kv_pages, "kv_pages"), _dev(block_table, "block_table"),
                                _dev(seq_lens, "seq_lens"), _dev(o, "o"), B, Hq, d_c, dk - d_c, page_size, mpps,
                                num_pages, float((128 + 64) ** -0.5 if scale is None else scale), num_splits,

@@ -53,7 +53,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_HEAD_DIM: return "ATTN_ERR_HEAD_DIM: head dimension must be 64 or 128";
     case ATTN_ERR_DTYPE: return "ATTN_ERR_DTYPE: unsupported element type";
     case ATTN_ERR_LAYOUT: return "ATTN_ERR_LAYOUT: unsupported layout";
-    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace missing or too small";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace too small";
     case ATTN_ERR_ALIGN: return "ATTN_ERR_ALIGN: tensor pointer not 16-byte aligned";
     case ATTN_ERR_LAUNCH: return "ATTN_ERR_LAUNCH: kernel launch failed";
     case ATTN_ERR_PAGE: return "ATTN_ERR_PAGE: page_size must be 16";
@@ -129,9 +129,11 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int d, int max_pages_p
 int attn_decode_ex(const void* q, const void* k_pages, const void* v_pages,
                    const int32_t* block_table, const int32_t* seq_lens, void* o,
                    int B, int Hq, int Hkv, int d, int page_size, int max_pages_per_seq,
-                   int num_pages, float scale, int num_splits, const attn_variant* variant,
-                   void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !o) return ATTN_ERR_NULL;
+                   int num_pages, float scale, int num_splits, int dtype,
+                   const attn_variant* variant, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !o || !workspace) return ATTN_ERR_NULL;
+  if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
   if (B < 1 || max_pages_per_seq < 1 || num_pages < 1 || num_splits < 0) return ATTN_ERR_SHAPE;
   int st = check_heads(Hq, Hkv);
   if (st) return st;
@@ -151,7 +153,7 @@ int attn_decode_ex(const void* q, const void* k_pages, const void* v_pages,
   const int S = num_splits > 0 ? attn_decode_num_splits(B, Hkv, max_pages_per_seq, num_splits)
                                : attn_decode_num_splits(B, Hkv, split_pages, 0);
   const size_t need = attn_decode_workspace_size(B, Hq, Hkv, d, max_pages_per_seq, num_splits);
-  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o) ||
       !aligned16(workspace) || (reinterpret_cast<uintptr_t>(block_table) & 3u) ||
       (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
@@ -177,10 +179,10 @@ int attn_decode_ex(const void* q, const void* k_pages, const void* v_pages,
 int attn_decode(const void* q, const void* k_pages, const void* v_pages,
                 const int32_t* block_table, const int32_t* seq_lens, void* o,
                 int B, int Hq, int Hkv, int d, int page_size, int max_pages_per_seq,
-                int num_pages, float scale, int num_splits,
+                int num_pages, float scale, int num_splits, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream) {
   return attn_decode_ex(q, k_pages, v_pages, block_table, seq_lens, o, B, Hq, Hkv, d, page_size,
-                        max_pages_per_seq, num_pages, scale, num_splits, nullptr, workspace,
+                        max_pages_per_seq, num_pages, scale, num_splits, dtype, nullptr, workspace,
                         workspace_bytes, stream);
 }
 
@@ -260,7 +262,7 @@ int attn_backward(const void* q, const void* k, const void* v, const void* o, co
                   const float* lse, void* dq, void* dk, void* dv, int B, int N, int Hq, int Hkv, int d,
                   float scale, int causal, int layout, void* workspace, size_t workspace_bytes,
                   void* stream) {
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return ATTN_ERR_NULL;
   if (B < 1 || N < 1) return ATTN_ERR_SHAPE;
   int st = check_heads(Hq, Hkv);
   if (st) return st;
@@ -270,7 +272,7 @@ int attn_backward(const void* q, const void* k, const void* v, const void* o, co
   if ((long long)B * N * Hq * d > kMaxElems) return ATTN_ERR_SHAPE;
   if ((long long)Hq * d >= (1 << 24)) return ATTN_ERR_SHAPE;  // row offsets in a tile fit 32 bits
   const size_t need = attn_backward_workspace_size(B, N, Hq);
-  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) ||
       (reinterpret_cast<uintptr_t>(lse) & 3u))
@@ -315,7 +317,7 @@ int attn_decode_mla(const void* q, const void* kv_pages, const int32_t* block_ta
                     void* o, int B, int Hq, int d_c, int d_r, int page_size, int max_pages_per_seq,
                     int num_pages, float scale, int num_splits, void* workspace, size_t workspace_bytes,
                     void* stream) {
-  if (!q || !kv_pages || !block_table || !seq_lens || !o) return ATTN_ERR_NULL;
+  if (!q || !kv_pages || !block_table || !seq_lens || !o || !workspace) return ATTN_ERR_NULL;
   if (B < 1 || Hq < 1 || max_pages_per_seq < 1 || num_pages < 1 || num_splits < 0) return ATTN_ERR_SHAPE;
   if (Hq % 16) return ATTN_ERR_SHAPE;
   if (d_c != 512 || d_r != 64) return ATTN_ERR_HEAD_DIM;
@@ -325,7 +327,7 @@ int attn_decode_mla(const void* q, const void* kv_pages, const int32_t* block_ta
   if ((long long)num_pages * page_size * 576 > kMaxElems || (long long)B * max_pages_per_seq > kMaxElems)
     return ATTN_ERR_SHAPE;
   const int S = attn_decode_mla_num_splits(B, Hq, max_pages_per_seq, num_splits);
-  if (!workspace || workspace_bytes < attn_decode_mla_workspace_size(B, Hq, max_pages_per_seq, num_splits))
+  if (workspace_bytes < attn_decode_mla_workspace_size(B, Hq, max_pages_per_seq, num_splits))
     return ATTN_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(kv_pages) || !aligned16(o) || !aligned16(workspace) ||
       (reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))

@@ -26,9 +26,10 @@
  *   [FA]    "inference-attention" (brunomaga.github.io), section "FlashAttention"
  *           (running max m, running sum l, unnormalised O rescaled by e^(m-m'),
  *           output O / l; tiles entirely above the diagonal are skipped) and
- *           section "FlashDecoding" (split the cached keys and values along the
- *           sequence, each chunk yields a partial output with its max and sum,
- *           a final reduction combines them with the same rescaling).
+ *           section "FlashDecoding" (the cached keys and values are cut into
+ *           ranges along the sequence; each range gives an unnormalised
+ *           partial output with its own max and sum, and one more pass merges
+ *           the partials after bringing them to a common max).
  *   [PAGED] "Module 09: Efficient Attention" (learnllm.pages.dev), section "Paged
  *           Attention: The KV Cache as Virtual Memory", subsection "Code: A
  *           Paged KV Cache from Scratch": pool (num_blocks, block_size,
@@ -74,7 +75,8 @@ enum {
     ATTN_ERR_HEAD_DIM = -4,   /* d is not 64 or 128 */
     ATTN_ERR_DTYPE = -5,      /* unsupported dtype code */
     ATTN_ERR_LAYOUT = -6,     /* unsupported layout code */
-    ATTN_ERR_WORKSPACE = -7,  /* workspace too small (or NULL when needed) */
+    ATTN_ERR_WORKSPACE = -7,  /* workspace_bytes below the size the call needs
+                                 (a NULL workspace is ATTN_ERR_NULL) */
     ATTN_ERR_ALIGN = -8,      /* a tensor pointer is not 16-byte aligned */
     ATTN_ERR_LAUNCH = -9,     /* the HIP runtime refused a launch */
     ATTN_ERR_PAGE = -10       /* page_size is not 16 */
@@ -157,9 +159,11 @@ int attn_prefill_ex(const void* q, const void* k, const void* v, void* o, float*
 int attn_decode_num_splits(int B, int Hkv, int max_pages_per_seq, int num_splits);
 
 /*
- * attn_decode_workspace_size - bytes of fp32 scratch attn_decode needs for
- * (B, Hq, d, num_splits) after resolving num_splits with
- * attn_decode_num_splits: B*Hq*num_splits*(d + 2)*4. Returns 0 for invalid sizes.
+ * attn_decode_workspace_size - bytes of fp32 scratch attn_decode needs:
+ * B*Hq*S*(d + 2)*4, with S = attn_decode_num_splits(B, Hkv, max_pages_per_seq,
+ * num_splits). It takes Hkv and max_pages_per_seq besides (B, Hq, d,
+ * num_splits) because the automatic split count (num_splits = 0) is a
+ * function of them. Returns 0 for invalid sizes.
  */
 size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int d, int max_pages_per_seq,
                                   int num_splits);
@@ -191,17 +195,26 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int d, int max_pages_p
  * result does not depend on where the pages sit in the pool: a permuted block
  * table gives output bit-identical to the identity table.
  *
+ * dtype:       element type of q, the pools and o. ATTN_BF16 is the one
+ *              supported (bf16 in, fp32 accumulation, bf16 out, the widening
+ *              policy of [SDPA] section 4); any other code returns
+ *              ATTN_ERR_DTYPE.
+ * workspace:   caller-owned device memory of at least
+ *              attn_decode_workspace_size(B, Hq, Hkv, d, max_pages_per_seq,
+ *              num_splits) bytes. It is needed for every split count (the
+ *              merge pass also runs for one split), so NULL returns
+ *              ATTN_ERR_NULL and a smaller size ATTN_ERR_WORKSPACE. Calls
+ *              that overlap in time must not share one.
+ *
  * Preconditions checked on the device side only by the caller:
  *   0 <= seq_lens[b] <= max_pages_per_seq * page_size, and every table entry
  *   that is read lies in [0, num_pages). Violations read out of bounds.
- * Requires page_size == 16, d in {64, 128}, Hq a multiple of Hkv,
- * workspace_bytes >= attn_decode_workspace_size(...). The workspace is caller
- * owned; calls that overlap in time must not share one.
+ * Requires page_size == 16, d in {64, 128}, Hq a multiple of Hkv.
  */
 int attn_decode(const void* q, const void* k_pages, const void* v_pages,
                 const int32_t* block_table, const int32_t* seq_lens, void* o,
                 int B, int Hq, int Hkv, int d, int page_size, int max_pages_per_seq,
-                int num_pages, float scale, int num_splits,
+                int num_pages, float scale, int num_splits, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -288,8 +301,9 @@ int attn_prefill_paged(const void* q, const void* k_pages, const void* v_pages,
 int attn_decode_ex(const void* q, const void* k_pages, const void* v_pages,
                    const int32_t* block_table, const int32_t* seq_lens, void* o,
                    int B, int Hq, int Hkv, int d, int page_size, int max_pages_per_seq,
-                   int num_pages, float scale, int num_splits, const attn_variant* variant,
-                   void* workspace, size_t workspace_bytes, void* stream);
+                   int num_pages, float scale, int num_splits, int dtype,
+                   const attn_variant* variant, void* workspace, size_t workspace_bytes,
+                   void* stream);
 
 /*
  * attn_backward_workspace_size - bytes of fp32 scratch attn_backward needs:
@@ -313,8 +327,8 @@ size_t attn_backward_workspace_size(int B, int N, int Hq);
  *                 (attn_prefill_ex with the same q, k, v, scale, causal).
  * dq, dk, dv:     outputs, fully overwritten (no accumulation into them).
  * workspace:      caller-owned device memory of at least
- *                 attn_backward_workspace_size(B, N, Hq) bytes; calls that
- *                 overlap in time must not share one.
+ *                 attn_backward_workspace_size(B, N, Hq) bytes (NULL returns
+ *                 ATTN_ERR_NULL); calls that overlap in time must not share one.
  * Requires d in {64, 128} and Hq a multiple of Hkv. Deterministic: every
  * gradient element is reduced in a fixed order (no atomics).
  */
@@ -349,7 +363,8 @@ size_t attn_decode_mla_workspace_size(int B, int Hq, int max_pages_per_seq, int 
  * scale:      the score scale of the heads the latent stands for, usually
  *             1/sqrt(d_head + d_r).
  * Requires d_c == 512, d_r == 64, Hq a multiple of 16, page_size == 16 and
- * workspace_bytes >= attn_decode_mla_workspace_size(...). Preconditions on
+ * workspace_bytes >= attn_decode_mla_workspace_size(...) (a NULL workspace
+ * returns ATTN_ERR_NULL). Preconditions on
  * device data as for attn_decode. The split boundaries depend only on L and
  * the split count, so a permuted table gives bit-identical output.
  */

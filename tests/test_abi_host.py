@@ -90,10 +90,10 @@ def test_prefill_plain_entry_validates(L):
 
 def decode(L, **kw):
     a = dict(q=A, k=A, v=A, table=A, lens=A, o=A, B=2, Hq=8, Hkv=2, d=128, page_size=16, mpps=4,
-             num_pages=8, scale=0.1, splits=0, ws=A, ws_bytes=1 << 30, var=None)
+             num_pages=8, scale=0.1, splits=0, dtype=1, ws=A, ws_bytes=1 << 30, var=None)
     a.update(kw)
     args = (a["q"], a["k"], a["v"], a["table"], a["lens"], a["o"], a["B"], a["Hq"], a["Hkv"],
-            a["d"], a["page_size"], a["mpps"], a["num_pages"], a["scale"], a["splits"])
+            a["d"], a["page_size"], a["mpps"], a["num_pages"], a["scale"], a["splits"], a["dtype"])
     if a["var"] is None:
         return L.attn_decode(*args, a["ws"], a["ws_bytes"], None)
     return L.attn_decode_ex(*args, a["var"], a["ws"], a["ws_bytes"], None)
@@ -104,7 +104,12 @@ def decode(L, **kw):
     (dict(B=0), "ATTN_ERR_SHAPE"), (dict(mpps=0), "ATTN_ERR_SHAPE"), (dict(num_pages=0), "ATTN_ERR_SHAPE"),
     (dict(splits=-1), "ATTN_ERR_SHAPE"), (dict(Hq=8, Hkv=3), "ATTN_ERR_GQA"), (dict(d=32), "ATTN_ERR_HEAD_DIM"),
     (dict(page_size=8), "ATTN_ERR_PAGE"), (dict(scale=float("nan")), "ATTN_ERR_SHAPE"),
-    (dict(ws=None), "ATTN_ERR_WORKSPACE"), (dict(ws_bytes=16), "ATTN_ERR_WORKSPACE"),
+    # the workspace is needed for every split count: NULL is ERR_NULL, too small ERR_WORKSPACE
+    (dict(ws=None), "ATTN_ERR_NULL"), (dict(ws=None, splits=1), "ATTN_ERR_NULL"),
+    (dict(ws_bytes=16), "ATTN_ERR_WORKSPACE"),
+    # bf16 is the one element type of the decode
+    (dict(dtype=0), "ATTN_ERR_DTYPE"), (dict(dtype=2), "ATTN_ERR_DTYPE"),
+    (dict(dtype=0, var=var(window=5)), "ATTN_ERR_DTYPE"),
     (dict(k=A + 4), "ATTN_ERR_ALIGN"), (dict(table=A + 2), "ATTN_ERR_ALIGN"),
     (dict(mpps=1 << 28), "ATTN_ERR_SHAPE"),
     (dict(var=var(window=-3)), "ATTN_ERR_SHAPE"), (dict(var=var(n_sink=2)), "ATTN_ERR_SHAPE"),
@@ -113,6 +118,13 @@ def decode(L, **kw):
 ])
 def test_decode_rejects(L, kw, err):
     assert decode(L, **kw) == ERR[err]
+
+
+def test_decode_accepts_bf16(L):
+    # ATTN_BF16 passes the dtype check: the call goes on to fail a later one
+    # (no kernel is launched in these host tests)
+    assert decode(L, dtype=1, ws_bytes=16) == ERR["ATTN_ERR_WORKSPACE"]
+    assert decode(L, dtype=1, var=var(window=5), k=A + 4) == ERR["ATTN_ERR_ALIGN"]
 
 
 def test_split_count_and_workspace_size(L):
@@ -202,7 +214,7 @@ def backward(L, **kw):
     (dict(do=None), "ATTN_ERR_NULL"), (dict(lse=None), "ATTN_ERR_NULL"), (dict(dv=None), "ATTN_ERR_NULL"),
     (dict(B=0), "ATTN_ERR_SHAPE"), (dict(N=0), "ATTN_ERR_SHAPE"), (dict(Hq=4, Hkv=3), "ATTN_ERR_GQA"),
     (dict(d=80), "ATTN_ERR_HEAD_DIM"), (dict(layout=5), "ATTN_ERR_LAYOUT"), (dict(scale=float("nan")), "ATTN_ERR_SHAPE"),
-    (dict(ws=None), "ATTN_ERR_WORKSPACE"), (dict(ws_bytes=8), "ATTN_ERR_WORKSPACE"), (dict(dk=A + 8), "ATTN_ERR_ALIGN"),
+    (dict(ws=None), "ATTN_ERR_NULL"), (dict(ws_bytes=8), "ATTN_ERR_WORKSPACE"), (dict(dk=A + 8), "ATTN_ERR_ALIGN"),
     (dict(lse=A + 2), "ATTN_ERR_ALIGN"),
 ])
 def test_backward_rejects(L, kw, err):
@@ -226,7 +238,7 @@ def mla(L, **kw):
 
 @pytest.mark.parametrize("kw,err", [
     (dict(kv=None), "ATTN_ERR_NULL"), (dict(table=None), "ATTN_ERR_NULL"), (dict(B=0), "ATTN_ERR_SHAPE"),
-    (dict(Hq=24), "ATTN_ERR_SHAPE"), (dict(d_c=256), "ATTN_ERR_HEAD_DIM"), (dict(d_r=32), "ATTN_ERR_HEAD_DIM"),
+    (dict(ws=None), "ATTN_ERR_NULL"), (dict(Hq=24), "ATTN_ERR_SHAPE"), (dict(d_c=256), "ATTN_ERR_HEAD_DIM"), (dict(d_r=32), "ATTN_ERR_HEAD_DIM"),
     (dict(page_size=64), "ATTN_ERR_PAGE"), (dict(scale=float("inf")), "ATTN_ERR_SHAPE"),
     (dict(ws_bytes=100), "ATTN_ERR_WORKSPACE"), (dict(o=A + 2), "ATTN_ERR_ALIGN"), (dict(splits=-1), "ATTN_ERR_SHAPE"),
 ])

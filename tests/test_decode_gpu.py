@@ -139,8 +139,29 @@ def full_size(x: wl.DecodeInputs, batches=None):
 
 
 def test_workload_4_full_size():
-    full_size(wl.workload_4(), batches=[0, 1, 17, 40, 63])
+    full_size(wl.workload_4())
 
 
 def test_workload_5_full_size():
     full_size(wl.workload_5())
+
+
+def test_launch_stream_other_than_the_current_one():
+    """The binding's own workspace belongs to the launch stream: after the call
+    returns, the next allocations on that stream are stream-ordered behind the
+    kernels. Here the decode runs on a side stream with no workspace passed,
+    and the side stream at once allocates and fills memory of the same size
+    many times; the output must still match the oracle."""
+    x = wl.paged_decode_inputs(3, 32, 8, 128, [4000, 17, 2500], seed=31)
+    q, kp, vp, bt, sl = to_gpu(x)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        o = torch.empty_like(q)
+    bd.attn_decode(q, kp, vp, bt, sl, o, scale=x.scale, num_splits=7, stream=side)
+    need = bd.attn_decode_workspace_size(x.B, x.Hq, x.Hkv, x.d, x.max_pages_per_seq, 7)
+    with torch.cuda.stream(side):
+        junk = [torch.full((need // 4 + 4,), float("nan"), device="cuda") for _ in range(4)]
+    torch.cuda.synchronize()
+    del junk
+    check(o.cpu(), oracle(x), "side stream")

@@ -1,7 +1,7 @@
 """Absorbed-MLA decode on the GPU (through the C ABI) against the CPU float64
 oracle: ragged lengths, an empty sequence, several split counts, head counts
 that leave waves idle, NaN-poisoned unused slots, a permuted table against the
-identity table (bit-exact), and sampled heads of the full-size workload.
+identity table (bit-exact), and the whole output of the full-size workload.
 
 Tolerance against the fp64 oracle: bf16 inputs, fp32 accumulation,
 max-abs <= 2e-2 and mean-abs <= 5e-3 (the outputs are convex combinations of
@@ -74,21 +74,13 @@ def test_mla_permuted_table_is_bit_identical_to_identity():
     assert torch.equal(ga.view(torch.int16), gb.view(torch.int16))
 
 
-def test_workload_7_full_size_sampled():
+def test_workload_7_full_size():
+    """Every head of every sequence of the full-size workload against the oracle."""
     x = wl.workload_7()
     log(f"case: {x.name}, seq_lens={x.seq_lens.tolist()}")
     got = run(x)
-    rng = np.random.default_rng(960)
-    kv = x.kv_pages.float().numpy()
-    worst = 0.0
-    for b in rng.choice(x.B, 4, replace=False):
-        L = int(x.seq_lens[b])
-        rows = ao.gather_kv_ref(kv, x.block_table[b].numpy(), L, 16).astype(np.float64)
-        for h in rng.choice(x.Hq, 3, replace=False):
-            s = rows @ ao.as_f64(x.q[b, h]) * x.scale
-            p = np.exp(s - s.max())
-            ref = (p / p.sum()) @ rows[:, :512]
-            e = np.abs(got[b, h].double().numpy() - ref).max()
-            worst = max(worst, e)
-            assert e <= BF16_MAX, (b, h, e)
-    log(f"  sampled max-abs {worst:.3e}")
+    assert bool(torch.isfinite(got.float()).all())
+    ref = ao.mla_decode_ref(x.q, x.kv_pages, x.block_table, x.seq_lens, x.scale, x.d_c)
+    e = np.abs(got.double().numpy() - ref)
+    log(f"  whole output: max-abs {e.max():.3e} mean-abs {e.mean():.3e}")
+    assert e.max() <= BF16_MAX and e.mean() <= BF16_MEAN

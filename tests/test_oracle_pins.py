@@ -448,15 +448,36 @@ def test_window_mask_matches_printed_grid():
     assert np.array_equal(ao.position_mask(np.arange(n), np.arange(n), n), np.tril(np.ones((n, n), bool)))
 
 
+def anchor_grids():
+    """(n, window, n_sink, grid) from the hand-written grids file."""
+    grids, cur = [], None
+    for line in golden_lines("anchor_window_mask.txt"):
+        if line.startswith("grid"):
+            f = dict(kv.split("=") for kv in line.split()[1:])
+            cur = [int(f["n"]), int(f["window"]), int(f["n_sink"]), []]
+            grids.append(cur)
+        else:
+            cur[3].append([int(c) for c in line.split()])
+    return [(n, W, S, np.array(g, dtype=bool)) for n, W, S, g in grids]
+
+
 def test_initial_tokens_stay_visible_with_a_window():
-    n, W, S = 9, 3, 2
-    got = ao.position_mask(np.arange(n), np.arange(n), W, S)
-    tri = np.tril(np.ones((n, n), bool))
-    band = np.triu(tri, -(W - 1))               # 0 <= i - j < W
-    anchors = tri & (np.arange(n)[None, :] < S)
-    assert np.array_equal(got, band | anchors)
+    grids = anchor_grids()
+    assert len(grids) == 3
+    for n, W, S, grid in grids:
+        assert grid.shape == (n, n)
+        assert np.array_equal(ao.position_mask(np.arange(n), np.arange(n), W, S), grid), (n, W, S)
+        # one query at a time (the decode form: the query at position t sees
+        # keys 0 .. t through the same rule) reproduces each row
+        for t in range(n):
+            assert np.array_equal(ao.position_mask([t], np.arange(t + 1), W, S)[0], grid[t, :t + 1])
+        # a chunk of rows after a prefix: positions, not row numbers, decide
+        P = n // 2
+        assert np.array_equal(ao.position_mask(P + np.arange(n - P), np.arange(n), W, S), grid[P:])
     with pytest.raises(ValueError):
         ao.position_mask(np.arange(3), np.arange(3), None, 1)
+    with pytest.raises(ValueError):
+        ao.position_mask(np.arange(3), np.arange(3), 0, 0)
 
 
 def test_sink_mass_matches_printed_closed_form():
@@ -518,8 +539,9 @@ def test_windowed_prefill_matches_torch_with_explicit_mask(W, S):
     B, Hq, Hkv, N, d = 2, 4, 2, 23, 8
     q, k, v = rnd((B, N, Hq, d), 150), rnd((B, N, Hkv, d), 151), rnd((B, N, Hkv, d), 152)
     o, lse = ao.prefill_variant_ref(q, k, v, 0.3, "BNHD", window=W, n_sink=S)
-    i, j = np.arange(N)[:, None], np.arange(N)[None, :]
-    m = torch.from_numpy(((j <= i) & (i - j < W)) | ((j <= i) & (j < S)))
+    # the mask itself is pinned by the printed and hand-written grids above;
+    # this checks the masked attention around it against torch
+    m = torch.from_numpy(ao.position_mask(np.arange(N), np.arange(N), W, S))
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a.transpose(0, 2, 1, 3)))
     want = F.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=m, scale=0.3,
                                           enable_gqa=True).numpy().transpose(0, 2, 1, 3)

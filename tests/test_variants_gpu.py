@@ -176,11 +176,10 @@ BENCH_W, BENCH_S = 1024, 4          # prefill: window and initial tokens
 BENCH_WD = 8192                     # decode: window
 
 
-def test_windowed_prefill_full_size_sampled():
+def test_windowed_prefill_full_size():
     """Headline prefill shape (B=4 N=4096 Hq=32 Hkv=8 d=128) with a 1024 window,
-    4 initial tokens and per-head sink logits, as timed: sampled rows (the
-    first row, both sides of the window's first full length, the last row and
-    random ones) against the oracle row by row."""
+    4 initial tokens and per-head sink logits, as timed: the whole output and
+    LSE against the oracle."""
     x = wl.workload_2()
     W, S = BENCH_W, BENCH_S
     sinks = torch.linspace(-1.0, 3.0, x.Hq, dtype=torch.float32)
@@ -190,28 +189,20 @@ def test_windowed_prefill_full_size_sampled():
                            sinks=sinks.cuda(), lse=lse)
     torch.cuda.synchronize()
     o, lse = o.cpu(), lse.cpu()
-    rng = np.random.default_rng(790)
-    worst = 0.0
-    keys = np.arange(x.N)
-    for b in range(x.B):
-        for i in [0, W - 1, W, W + 1, x.N - 1] + rng.integers(0, x.N, 3).tolist():
-            h = int(rng.integers(0, x.Hq))
-            kv = ao.kv_head_of(h, x.Hq, x.Hkv)
-            allowed = ao.position_mask([i], keys, window=W, n_sink=S)
-            ref, ref_lse = ao.sdpa_masked_ref(x.q[b, i, h][None, None], x.k[b, :, kv][None], x.v[b, :, kv][None],
-                                              x.scale, allowed, sinks=sinks[h:h + 1].numpy())
-            e = np.abs(o[b, i, h].double().numpy() - ref[0, 0]).max()
-            worst = max(worst, e)
-            assert e <= BF16_MAX, (b, i, h, e)
-            assert abs(float(lse[b, h, i]) - ref_lse[0, 0]) <= LSE_BF16, (b, i, h)
-    log(f"  sampled max-abs {worst:.3e}")
+    ref, ref_lse = ao.prefill_variant_ref(x.q, x.k, x.v, x.scale, "BNHD", window=W, n_sink=S,
+                                          sinks=sinks.numpy())
+    e = np.abs(o.double().numpy() - ref)
+    le = float(np.abs(lse.double().numpy() - ref_lse).max())
+    log(f"  whole output: max-abs {e.max():.3e} mean-abs {e.mean():.3e}; lse max-abs {le:.3e}")
+    assert e.max() <= BF16_MAX and e.mean() <= BF16_MEAN
+    assert le <= LSE_BF16
 
 
-def test_windowed_decode_full_size_sampled():
+def test_windowed_decode_full_size():
     """Long-context paged decode (B=4 Hq=64 Hkv=8 d=128, 96K-128K tokens,
     permuted pages) with an 8192 window, 4 initial tokens and per-head sink
-    logits, as timed. The oracle reads only the visible tokens (the anchors
-    and the window), gathered through the block table here."""
+    logits, as timed: every head of every sequence against the oracle's
+    windowed decode."""
     x = wl.workload_5()
     W, S = BENCH_WD, BENCH_S
     sinks = torch.linspace(-1.0, 3.0, x.Hq, dtype=torch.float32)
@@ -221,21 +212,8 @@ def test_windowed_decode_full_size_sampled():
     torch.cuda.synchronize()
     o = o.cpu()
     assert bool(torch.isfinite(o.float()).all())
-    rng = np.random.default_rng(791)
-    worst = 0.0
-    for b in range(x.B):
-        L = int(x.seq_lens[b])
-        pos = np.arange(L)
-        vis = pos[ao.position_mask([L - 1], pos, window=W, n_sink=S)[0]]
-        pages = x.block_table[b].numpy()[vis // x.page_size]
-        slots = vis % x.page_size
-        for h in [0, x.Hq - 1] + rng.integers(0, x.Hq, 4).tolist():
-            kv = ao.kv_head_of(h, x.Hq, x.Hkv)
-            K = x.k_pages[pages, slots, kv].float().numpy()
-            V = x.v_pages[pages, slots, kv].float().numpy()
-            ref, _ = ao.sdpa_masked_ref(x.q[b, h][None, None], K[None], V[None], x.scale,
-                                        np.ones((1, len(vis)), dtype=bool), sinks=sinks[h:h + 1].numpy())
-            e = np.abs(o[b, h].double().numpy() - ref[0, 0]).max()
-            worst = max(worst, e)
-            assert e <= BF16_MAX, (b, h, e)
-    log(f"  sampled max-abs {worst:.3e}")
+    ref = ao.decode_ref(x.q, x.k_pages, x.v_pages, x.block_table, x.seq_lens, x.scale,
+                        window=W, n_sink=S, sinks=sinks.numpy())
+    e = np.abs(o.double().numpy() - ref)
+    log(f"  whole output: max-abs {e.max():.3e} mean-abs {e.mean():.3e}")
+    assert e.max() <= BF16_MAX and e.mean() <= BF16_MEAN
