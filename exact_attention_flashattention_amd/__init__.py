@@ -8,7 +8,7 @@ computes attention on the CPU.
 """
 from .binding import (  # noqa: F401
     AttnError, AttnLibraryMissing, AttnVariant, LIB_PATH, attn_backward, attn_backward_workspace_size,
-    attn_decode, attn_decode_ex, attn_decode_mla, attn_decode_mla_num_splits, attn_decode_mla_workspace_size,
+    attn_decode, attn_decode_ex, attn_decode_mla, attn_decode_noalloc, attn_decode_mla_num_splits, attn_decode_mla_workspace_size,
     attn_decode_num_splits,
     attn_decode_workspace_size, attn_gather_pages, attn_kv_append, attn_prefill, attn_prefill_ex,
     attn_prefill_paged, attn_status_string, lib,

@@ -37,6 +37,7 @@ SIGNATURES = [
                          _vp]),
     ("attn_decode_ex", _i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _var, _vp,
                             _sz, _vp]),
+    ("attn_decode_noalloc", _i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]),
     ("attn_kv_append", _i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
     ("attn_prefill_paged", _i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                                 _i, _i, _f, _var, _vp]),
@@ -261,6 +262,36 @@ def _decode(q, k_pages, v_pages, block_table, seq_lens, o, scale, num_splits, wo
         var, _keep = _variant(*variant, Hq)
         st = lib().attn_decode_ex(*args, var, *tail)
         _check(st, "attn_decode_ex")
+    return o
+
+
+ATTN_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def attn_decode_noalloc(q, k_pages, v_pages, block_table, seq_lens, o, *, scale: Optional[float] = None,
+                        num_splits: int = 0, stream=None):
+    """attn_decode whose split partials go to the library's fixed per-GPU
+    scratch (no workspace, nothing allocated by the call); o [B, Hq, d] bf16
+    must be passed. Calls that overlap in time on one GPU must not be issued."""
+    import torch
+    if q.dtype != torch.bfloat16 or k_pages.dtype != torch.bfloat16 or v_pages.dtype != torch.bfloat16:
+        raise ValueError("decode takes bf16 q and pools")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    B, Hq, d = q.shape
+    num_pages, page_size, Hkv, d2 = k_pages.shape
+    if d2 != d or v_pages.shape != k_pages.shape:
+        raise ValueError("pool shape mismatch")
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_table must be [B, max_pages] and seq_lens [B]")
+    if o is None or o.shape != q.shape or o.dtype != q.dtype:
+        raise ValueError("o must be given, bf16 [B, Hq, d]")
+    st = lib().attn_decode_noalloc(_dev(q, "q"), _dev(k_pages, "k_pages"), _dev(v_pages, "v_pages"),
+                                   _dev(block_table, "block_table"), _dev(seq_lens, "seq_lens"), _dev(o, "o"),
+                                   B, Hq, Hkv, d, page_size, block_table.shape[1], num_pages,
+                                   float(d ** -0.5 if scale is None else scale), num_splits, ATTN_BF16,
+                                   _stream(stream))
+    _check(st, "attn_decode_noalloc")
     return o
 
 

@@ -7,6 +7,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace {
 
 constexpr long long kMaxElems = 1LL << 40;  // sanity bound on any one tensor
@@ -38,6 +40,44 @@ void set_variant(attn::PrefillParams& p, const attn_variant* v) {
   p.sinks = v ? v->sinks : nullptr;
 }
 
+// ---- fixed scratch of attn_decode_noalloc ----------------------------------------
+// The split partials of attn_decode_noalloc live in this array instead of a
+// caller-supplied workspace. Each GPU the library runs on holds its own copy
+// until the process ends. In host code `scratch` is only a stand-in for the
+// symbol: its device address is taken once per device with
+// hipGetSymbolAddress and kept in scratch_ptr, which is what kernels receive.
+constexpr size_t kScratchBytes = ATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the device `stream` belongs to (the current
+// device for the null stream); ATTN_ERR_LAUNCH if the runtime refuses.
+int device_scratch(hipStream_t stream, void** out) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return ATTN_ERR_LAUNCH;
+  int dev = cur;
+  if (stream) {
+    hipDevice_t sd;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess) return ATTN_ERR_LAUNCH;
+    dev = (int)sd;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    // the symbol's address is per device: take it with that device current
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return ATTN_ERR_LAUNCH;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !ptr) return ATTN_ERR_LAUNCH;
+    scratch_ptr[dev] = ptr;
+  }
+  *out = scratch_ptr[dev];
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -57,6 +97,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_ALIGN: return "ATTN_ERR_ALIGN: tensor pointer not 16-byte aligned";
     case ATTN_ERR_LAUNCH: return "ATTN_ERR_LAUNCH: kernel launch failed";
     case ATTN_ERR_PAGE: return "ATTN_ERR_PAGE: page_size must be 16";
+    case ATTN_ERR_SCRATCH: return "ATTN_ERR_SCRATCH: the call needs more than the fixed scratch of attn_decode_noalloc";
     default: return "unknown attn status";
   }
 }
@@ -126,13 +167,18 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int d, int max_pages_p
   return (size_t)B * Hq * S * (d + 2) * sizeof(float);
 }
 
-int attn_decode_ex(const void* q, const void* k_pages, const void* v_pages,
-                   const int32_t* block_table, const int32_t* seq_lens, void* o,
-                   int B, int Hq, int Hkv, int d, int page_size, int max_pages_per_seq,
-                   int num_pages, float scale, int num_splits, int dtype,
-                   const attn_variant* variant, void* workspace, size_t workspace_bytes,
-                   void* stream) {
-  if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !o || !workspace) return ATTN_ERR_NULL;
+// Validation and launch shared by attn_decode_ex and attn_decode_noalloc.
+// With fixed_scratch the workspace is the library's own array: its size
+// limit replaces workspace_bytes, and its device address is taken only once
+// every argument has passed.
+static int decode_enqueue(const void* q, const void* k_pages, const void* v_pages,
+                          const int32_t* block_table, const int32_t* seq_lens, void* o,
+                          int B, int Hq, int Hkv, int d, int page_size, int max_pages_per_seq,
+                          int num_pages, float scale, int num_splits, int dtype,
+                          const attn_variant* variant, void* workspace, size_t workspace_bytes,
+                          bool fixed_scratch, void* stream) {
+  if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !o) return ATTN_ERR_NULL;
+  if (!fixed_scratch && !workspace) return ATTN_ERR_NULL;
   if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
   if (B < 1 || max_pages_per_seq < 1 || num_pages < 1 || num_splits < 0) return ATTN_ERR_SHAPE;
   int st = check_heads(Hq, Hkv);
@@ -153,13 +199,21 @@ int attn_decode_ex(const void* q, const void* k_pages, const void* v_pages,
   const int S = num_splits > 0 ? attn_decode_num_splits(B, Hkv, max_pages_per_seq, num_splits)
                                : attn_decode_num_splits(B, Hkv, split_pages, 0);
   const size_t need = attn_decode_workspace_size(B, Hq, Hkv, d, max_pages_per_seq, num_splits);
-  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (fixed_scratch) {
+    if (need > kScratchBytes) return ATTN_ERR_SCRATCH;
+  } else if (workspace_bytes < need) {
+    return ATTN_ERR_WORKSPACE;
+  }
   if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o) ||
-      !aligned16(workspace) || (reinterpret_cast<uintptr_t>(block_table) & 3u) ||
+      (!fixed_scratch && !aligned16(workspace)) || (reinterpret_cast<uintptr_t>(block_table) & 3u) ||
       (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
     return ATTN_ERR_ALIGN;
   st = check_variant(variant, 1);
   if (st) return st;
+  if (fixed_scratch) {
+    st = device_scratch(reinterpret_cast<hipStream_t>(stream), &workspace);
+    if (st) return st;
+  }
 
   attn::DecodeParams p = {};
   p.q = q; p.k_pages = k_pages; p.v_pages = v_pages;
@@ -176,14 +230,34 @@ int attn_decode_ex(const void* q, const void* k_pages, const void* v_pages,
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+int attn_decode_ex(const void* q, const void* k_pages, const void* v_pages,
+                   const int32_t* block_table, const int32_t* seq_lens, void* o,
+                   int B, int Hq, int Hkv, int d, int page_size, int max_pages_per_seq,
+                   int num_pages, float scale, int num_splits, int dtype,
+                   const attn_variant* variant, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  return decode_enqueue(q, k_pages, v_pages, block_table, seq_lens, o, B, Hq, Hkv, d, page_size,
+                        max_pages_per_seq, num_pages, scale, num_splits, dtype, variant, workspace,
+                        workspace_bytes, false, stream);
+}
+
 int attn_decode(const void* q, const void* k_pages, const void* v_pages,
                 const int32_t* block_table, const int32_t* seq_lens, void* o,
                 int B, int Hq, int Hkv, int d, int page_size, int max_pages_per_seq,
                 int num_pages, float scale, int num_splits, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream) {
-  return attn_decode_ex(q, k_pages, v_pages, block_table, seq_lens, o, B, Hq, Hkv, d, page_size,
+  return decode_enqueue(q, k_pages, v_pages, block_table, seq_lens, o, B, Hq, Hkv, d, page_size,
                         max_pages_per_seq, num_pages, scale, num_splits, dtype, nullptr, workspace,
-                        workspace_bytes, stream);
+                        workspace_bytes, false, stream);
+}
+
+int attn_decode_noalloc(const void* q, const void* k_pages, const void* v_pages,
+                        const int32_t* block_table, const int32_t* seq_lens, void* o,
+                        int B, int Hq, int Hkv, int d, int page_size, int max_pages_per_seq,
+                        int num_pages, float scale, int num_splits, int dtype, void* stream) {
+  return decode_enqueue(q, k_pages, v_pages, block_table, seq_lens, o, B, Hq, Hkv, d, page_size,
+                        max_pages_per_seq, num_pages, scale, num_splits, dtype, nullptr, nullptr, 0,
+                        true, stream);
 }
 
 int attn_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_pages,

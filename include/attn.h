@@ -42,7 +42,8 @@
  * Conventions for every call:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
  *     allocates no device memory, keeps no pointer after the call returns and
- *     has no global state. Calls are thread-safe.
+ *     has no global state, with one exception: the fixed per-device scratch
+ *     array of attn_decode_noalloc (see there). Calls are thread-safe.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). The
  *     call validates its arguments on the host, enqueues its kernels on
  *     `stream` and returns without synchronising. Errors inside kernels (a
@@ -79,7 +80,9 @@ enum {
                                  (a NULL workspace is ATTN_ERR_NULL) */
     ATTN_ERR_ALIGN = -8,      /* a tensor pointer is not 16-byte aligned */
     ATTN_ERR_LAUNCH = -9,     /* the HIP runtime refused a launch */
-    ATTN_ERR_PAGE = -10       /* page_size is not 16 */
+    ATTN_ERR_PAGE = -10,      /* page_size is not 16 */
+    ATTN_ERR_SCRATCH = -11    /* attn_decode_noalloc: the call needs more
+                                 scratch than ATTN_NOALLOC_SCRATCH_BYTES */
 };
 
 /* Element types. */
@@ -216,6 +219,32 @@ int attn_decode(const void* q, const void* k_pages, const void* v_pages,
                 int B, int Hq, int Hkv, int d, int page_size, int max_pages_per_seq,
                 int num_pages, float scale, int num_splits, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_noalloc - attn_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation, kernels and results as attn_decode
+ * with the same arguments, but the split partials go to a scratch array of
+ * ATTN_NOALLOC_SCRATCH_BYTES (16 MiB) that the library holds on each GPU it
+ * runs on, from the first call on that GPU until the process ends. The call
+ * itself allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine); the caller still owns q, the pools, the table, seq_lens and o.
+ *
+ * Returns ATTN_ERR_SCRATCH when attn_decode_workspace_size(B, Hq, Hkv, d,
+ * max_pages_per_seq, num_splits) exceeds ATTN_NOALLOC_SCRATCH_BYTES (the
+ * long-context and batched decode shapes of the benchmarks need 8.5 MB and
+ * 4.3 MB), otherwise the statuses of attn_decode. The array is found on the
+ * device `stream` belongs to (the current device for the null stream).
+ * Every partial the merge reads is written by the same call first, so the
+ * array needs no clearing between calls. All calls on one GPU share its
+ * array: calls that overlap in time on one GPU (two streams, two threads)
+ * race on it and must be ordered by the caller.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int attn_decode_noalloc(const void* q, const void* k_pages, const void* v_pages,
+                        const int32_t* block_table, const int32_t* seq_lens, void* o,
+                        int B, int Hq, int Hkv, int d, int page_size, int max_pages_per_seq,
+                        int num_pages, float scale, int num_splits, int dtype, void* stream);
 
 /*
  * attn_kv_append - write the keys and values of new tokens into the paged

@@ -32,14 +32,14 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = header_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(L, n), n
     assert sorted(n for n, _, _ in binding.SIGNATURES) == names
 
 
 def test_status_strings_and_version(L):
-    for code in range(0, -11, -1):
+    for code in range(0, -12, -1):
         s = binding.status_string(code)
         assert s and "unknown" not in s
     assert "unknown" in binding.status_string(-99)
@@ -52,7 +52,7 @@ BUF = (ctypes.c_uint8 * 4096)()
 A = (ctypes.addressof(BUF) + 15) & ~15
 ERR = {n: header_enum(n) for n in ("ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_GQA", "ATTN_ERR_HEAD_DIM",
                                   "ATTN_ERR_DTYPE", "ATTN_ERR_LAYOUT", "ATTN_ERR_WORKSPACE",
-                                  "ATTN_ERR_ALIGN", "ATTN_ERR_PAGE")}
+                                  "ATTN_ERR_ALIGN", "ATTN_ERR_PAGE", "ATTN_ERR_SCRATCH")}
 
 
 def prefill(L, **kw):
@@ -125,6 +125,42 @@ def test_decode_accepts_bf16(L):
     # (no kernel is launched in these host tests)
     assert decode(L, dtype=1, ws_bytes=16) == ERR["ATTN_ERR_WORKSPACE"]
     assert decode(L, dtype=1, var=var(window=5), k=A + 4) == ERR["ATTN_ERR_ALIGN"]
+
+
+def noalloc(L, **kw):
+    a = dict(q=A, k=A, v=A, table=A, lens=A, o=A, B=2, Hq=8, Hkv=2, d=128, page_size=16, mpps=4,
+             num_pages=8, scale=0.1, splits=0, dtype=1)
+    a.update(kw)
+    return L.attn_decode_noalloc(a["q"], a["k"], a["v"], a["table"], a["lens"], a["o"], a["B"], a["Hq"],
+                                 a["Hkv"], a["d"], a["page_size"], a["mpps"], a["num_pages"], a["scale"],
+                                 a["splits"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,err", [
+    (dict(q=None), "ATTN_ERR_NULL"), (dict(o=None), "ATTN_ERR_NULL"), (dict(dtype=0), "ATTN_ERR_DTYPE"),
+    (dict(B=0), "ATTN_ERR_SHAPE"), (dict(Hq=8, Hkv=3), "ATTN_ERR_GQA"), (dict(d=32), "ATTN_ERR_HEAD_DIM"),
+    (dict(page_size=8), "ATTN_ERR_PAGE"), (dict(k=A + 4), "ATTN_ERR_ALIGN"),
+    # 64 * 64 * 100 splits * 130 floats is 213 MB, past the 16 MiB scratch
+    (dict(B=64, Hq=64, Hkv=8, mpps=1000, splits=100), "ATTN_ERR_SCRATCH"),
+])
+def test_decode_noalloc_rejects(L, kw, err):
+    # every refusal happens on the host, before the scratch address is taken
+    assert noalloc(L, **kw) == ERR[err]
+
+
+def test_noalloc_scratch_limit_matches_the_workspace_rule(L):
+    limit = 16 << 20
+    assert binding.ATTN_NOALLOC_SCRATCH_BYTES == limit
+    # the benchmark's long-context and batched decode shapes fit
+    assert L.attn_decode_workspace_size(4, 64, 8, 128, 8192, 0) <= limit
+    assert L.attn_decode_workspace_size(64, 32, 8, 128, 512, 0) <= limit
+    # the first split count past the limit is refused; the largest one that
+    # fits passes the size check and fails the alignment check after it
+    B, Hq, Hkv, d, mpps = 8, 64, 8, 128, 4096
+    per_split = B * Hq * (d + 2) * 4
+    s_max = limit // per_split
+    assert noalloc(L, B=B, Hq=Hq, Hkv=Hkv, d=d, mpps=mpps, splits=s_max + 1) == ERR["ATTN_ERR_SCRATCH"]
+    assert noalloc(L, B=B, Hq=Hq, Hkv=Hkv, d=d, mpps=mpps, splits=s_max, k=A + 4) == ERR["ATTN_ERR_ALIGN"]
 
 
 def test_split_count_and_workspace_size(L):
