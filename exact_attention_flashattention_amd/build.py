@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libattn.so")
-SOURCES = ["attn_abi.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "kv_append.hip", "backward_bf16.hip", "decode_mla.hip"]
+SOURCES = ["attn_abi.hip", "prefill_bf16.hip", "prefill_pp.hip", "prefill_f32.hip", "decode.hip", "kv_append.hip", "backward_bf16.hip", "decode_mla.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU instructions are kept out of the generated code (the

@@ -97,6 +97,7 @@ hipError_t launch_decode_mla(const MlaParams& p, hipStream_t stream);
 int mla_auto_splits(int B, int Hq, int max_pages_per_seq);
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream);
+hipError_t launch_prefill_pp(const PrefillParams& p, int d, int n_rows, bool paged, hipStream_t stream);
 hipError_t launch_backward(const BwdParams& p, int d, hipStream_t stream);
 hipError_t launch_prefill_paged(const PrefillParams& p, int d, int max_q_len, hipStream_t stream);
 hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_pages,

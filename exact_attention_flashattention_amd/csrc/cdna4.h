@@ -78,6 +78,26 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((NCNT & 15) | ((NCNT >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// s_waitcnt lgkmcnt(n) with the other counters left alone
+template <int NCNT>
+__device__ __forceinline__ void wait_lgkmcnt() {
+  static_assert(NCNT >= 0 && NCNT < 16, "lgkmcnt range");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (NCNT << 8));
+}
+
+// Work-group barrier without the release/acquire fences of __syncthreads():
+// those fences make the compiler wait for every HBM -> LDS copy in flight
+// (vmcnt(0)) at each barrier, which would drain a ring of prefetched tiles.
+// The caller waits explicitly for what must be complete (its own copies of
+// the tiles about to be read, its own LDS reads of buffers about to be
+// overwritten). The empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void barrier_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 // Work-group id -> work item such that each of the 8 XCDs (which receive

@@ -467,7 +467,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
       wait_vmcnt<kLoadsPerTile>();
     else
       wait_vmcnt<0>();
-    __syncthreads();
+    wait_lgkmcnt<0>();  // this wave's reads of the buffer the next copy overwrites
+    barrier_nofence();
   };
   // b_issue: buffer receiving tile j+3; b_k: K tile of tile j+1; b_v: V tile of tile j.
   // The scores of tile j were computed in the previous iteration, so their
@@ -594,13 +595,19 @@ hipError_t launch_cfg(const PrefillParams& p, int n_rows, hipStream_t stream) {
 #define ATTN_PREFILL_D64 8, 32
 #endif
 
+#ifndef ATTN_PREFILL_PINGPONG
+#define ATTN_PREFILL_PINGPONG 0
+#endif
+
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream) {
+  if (ATTN_PREFILL_PINGPONG) return launch_prefill_pp(p, d, p.N, false, stream);
   if (d == 128) return launch_cfg<128, ATTN_PREFILL_D128, false>(p, p.N, stream);
   if (d == 64) return launch_cfg<64, ATTN_PREFILL_D64, false>(p, p.N, stream);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill_paged(const PrefillParams& p, int d, int max_q_len, hipStream_t stream) {
+  if (ATTN_PREFILL_PINGPONG) return launch_prefill_pp(p, d, max_q_len, true, stream);
   if (d == 128) return launch_cfg<128, ATTN_PREFILL_D128, true>(p, max_q_len, stream);
   if (d == 64) return launch_cfg<64, ATTN_PREFILL_D64, true>(p, max_q_len, stream);
   return hipErrorInvalidValue;
