@@ -58,6 +58,9 @@ namespace {
 
 using namespace cdna4;
 
+#ifndef ATTN_PP_RING
+#define ATTN_PP_RING 6
+#endif
 constexpr int kPage = 16;           // tokens per page of a paged KV cache
 constexpr float kRescaleTau = 8.0f; // lazy-rescale threshold, base-2 exponent units
 
@@ -76,7 +79,8 @@ struct PP {
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;           // rows per 1 KiB copy instruction
   static constexpr int TILE = BN * ROWB;         // bytes of one K (or V) tile
-  static constexpr int RING = 6;                 // buffers per ring
+  static constexpr int RING = ATTN_PP_RING;      // buffers per ring
+  static constexpr int VMW = 2 * (RING - 3);     // copies a wave may leave in flight at a barrier
   static constexpr int VBASE = RING * TILE;      // V ring after the K ring
   static constexpr int OROW = D * 2 + 16;        // padded bytes per staged output row
   static constexpr int LDS_BYTES = (2 * VBASE > NW * 32 * OROW) ? 2 * VBASE : NW * 32 * OROW;
@@ -172,7 +176,11 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillParams p, int
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
   // a learned sink logit s_h enters as the initial state m = s_h, l = 1, O = 0
-  float m_ref = kNegInf, l_run = 0.f;
+  // m_ref starts at the most negative finite float ("no key yet"): a row
+  // max of -inf (every key masked) never moves it and s*c2 - m_ref stays
+  // -inf for masked scores, so no -inf guards are needed; the first finite
+  // row max always moves it (then the rescale factor is exactly 0).
+  float m_ref = -3.402823466e38f, l_run = 0.f;
   if (p.sinks) {
     m_ref = p.sinks[h] * 1.4426950408889634f;
     l_run = h2 == 0 ? 1.f : 0.f;  // the two lane halves' sums are added at the end
@@ -301,6 +309,25 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillParams p, int
       }
   };
 
+  // one operand of each, for the hand-ordered matrix phase
+  auto read_k_op = [&](const unsigned char* __restrict__ kt, int i) __attribute__((always_inline)) {
+    const int kb = i / C::KS, s_ = i % C::KS;
+    kreg[i] = *(const u32x4_t*)(kt + kpart[s_] + kb * 32 * C::ROWB);
+  };
+  auto read_v_op = [&](const unsigned char* __restrict__ vt, int i) __attribute__((always_inline)) {
+    const int ps = i / C::DB, db = i % C::DB;
+    u32x4_t a;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const s16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4_t*)(vt + vpart[r][db] + ps * 16 * C::ROWB));
+      const u32x2_t xx = __builtin_bit_cast(u32x2_t, x);
+      a[2 * r] = xx[0];
+      a[2 * r + 1] = xx[1];
+    }
+    vreg[i] = a;
+  };
+
   // ---- the steps of a tile -------------------------------------------------------
   // S^T = K Q^T from the K operands in kv
   auto gemm0 = [&](f32x16_t (&s)[C::KB]) __attribute__((always_inline)) {
@@ -322,10 +349,15 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillParams p, int
   };
   // key k0 + h2*4 + off (off a constant per element) is visible iff off <= lim
   // and, with a window, off >= lo or it is one of the n_sink initial positions
+  // First slot whose tile reaches past the causal limit of the wave's first
+  // row or past the end of the sequence (tiles are visited in increasing
+  // order, so every later slot needs the mask too); window edges are tested
+  // per slot.
+  const int t_mask = min(p.causal ? (P + qw0 + 1) / BN : k_tiles, Nk / BN);
+  const int mask_from = t_mask < sink_tiles ? t_mask : sink_tiles + max(t_mask - win_lo, 0);
   auto mask = [&](int t, f32x16_t (&s)[C::KB]) __attribute__((always_inline)) {
     const int k0 = tile_of(t) * BN;
-    const bool win_cut = W > 0 && k0 < P + qw0 + 31 - W + 1 && k0 + BN > p.n_sink;
-    if ((p.causal && k0 + BN - 1 > P + qw0) || (k0 + BN > Nk) || win_cut) {
+    if (t >= mask_from || (W > 0 && k0 < P + qw0 + 31 - W + 1 && k0 + BN > p.n_sink)) {
       const int base = k0 + h2 * 4;
       const int lim = (p.causal ? min(P + qi, Nk - 1) : Nk - 1) - base;
       const int lo = W > 0 ? P + qi - W + 1 - base : -BN;
@@ -341,7 +373,6 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillParams p, int
   };
   // row max, the lazy move of the reference m (per row), then s := s*c2 - m
   float m_old = m_ref;
-  bool moved = false;
   auto alu0 = [&](f32x16_t (&s)[C::KB]) __attribute__((always_inline)) {
     float rm[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
@@ -349,20 +380,21 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillParams p, int
 #pragma unroll
       for (int e = 0; e < 16; ++e) rm[e & 3] = fmaxf(rm[e & 3], s[kb][e]);
     const float mr = halves_max(fmaxf(fmaxf(rm[0], rm[1]), fmaxf(rm[2], rm[3])));
-    const float mt = (mr == kNegInf) ? kNegInf : mr * c2;
+    const float mt = mr * c2;  // c2 > 0: -inf stays -inf
     m_old = m_ref;
-    moved = mt > m_ref + kRescaleTau;
-    m_ref = moved ? mt : m_ref;
-    const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
+    m_ref = mt > m_ref + kRescaleTau ? mt : m_ref;
+    const float neg_m = -m_ref;
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[kb][e] = fmaf(s[kb][e], c2, neg_m);
   };
-  // rescale O and l for the rows whose reference moved (rare)
+  // rescale O and l for the rows whose reference moved (rare); a move always
+  // changes m_ref, so the test needs only the two references
   auto rescale = [&]() __attribute__((always_inline)) {
-    if (__builtin_amdgcn_ballot_w64(moved)) {
-      const float alpha = moved ? __builtin_amdgcn_exp2f(m_old - m_ref) : 1.f;
+    const bool mv = m_ref != m_old;
+    if (__builtin_amdgcn_ballot_w64(mv)) {
+      const float alpha = mv ? __builtin_amdgcn_exp2f(m_old - m_ref) : 1.f;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
@@ -390,6 +422,36 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillParams p, int
     }
     l_run += rs0 + rs1;
   };
+  // The common case: no score of this lane's keys is more than 2^8 above the
+  // reference (the lazy rule's test, taken on the lane's own 16 or 32 keys
+  // and combined across the wave), so the reference stays and the row max
+  // across the two lane halves is not needed; then s := s*c2 - m.
+  auto keep_ref = [&](const f32x16_t (&s)[C::KB]) __attribute__((always_inline)) {
+    float rm[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) rm[e & 3] = fmaxf(rm[e & 3], s[kb][e]);
+    const float mx = fmaxf(fmaxf(rm[0], rm[1]), fmaxf(rm[2], rm[3]));
+    return !__builtin_amdgcn_ballot_w64(mx * c2 > m_ref + kRescaleTau);
+  };
+  // the lazy move of the reference from the row max (both lane halves)
+  auto move_ref = [&](const f32x16_t (&s)[C::KB]) __attribute__((always_inline)) {
+    float rm[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) rm[e & 3] = fmaxf(rm[e & 3], s[kb][e]);
+    const float mt = halves_max(fmaxf(fmaxf(rm[0], rm[1]), fmaxf(rm[2], rm[3]))) * c2;
+    m_ref = mt > m_ref + kRescaleTau ? mt : m_ref;
+  };
+  auto shift = [&](f32x16_t (&s)[C::KB]) __attribute__((always_inline)) {
+    const float neg_m = -m_ref;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[kb][e] = fmaf(s[kb][e], c2, neg_m);
+  };
   u32x4_t pop[C::PS];  // P of the current slot, bf16 pairs in B-operand order
   auto bar = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
@@ -410,14 +472,21 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillParams p, int
   };
 
   // ---- prologue --------------------------------------------------------------------
-  // Copies of V_0..V_4 and K_0..K_5, then the softmax of slot 0 and the
-  // operands of slot 0's P V and slot 1's scores.
+  // Copies of K_0..K_5 and V_0..V_4 in the order the slots need them (K_0,
+  // K_1, V_0, then K_t, V_{t-1}); the wait covers only the first three (and
+  // the Q loads before them): the softmax of slot 0 and the operands of slot
+  // 0's P V and slot 1's scores. Each later matrix phase finds the tiles it
+  // reads complete under the loop's own vmcnt rule.
   f32x16_t sc[C::KB];
+  copy_tile(kg, 0, kbuf(0));
+  copy_tile(kg, 1, kbuf(1));
+  copy_tile(vg, 0, vbuf(0));
 #pragma unroll
-  for (int t = 0; t < 5; ++t) copy_tile(vg, t, vbuf(t));
-#pragma unroll
-  for (int t = 0; t < 6; ++t) copy_tile(kg, t, kbuf(t));
-  wait_vmcnt<0>();
+  for (int t = 2; t < C::RING; ++t) {
+    copy_tile(kg, t, kbuf(t));
+    copy_tile(vg, t - 1, vbuf(t - 1));
+  }
+  wait_vmcnt<2 * C::RING - 4>();
   bar();
   if (gf == 0 && ge > 0) {
     read_k(kbuf(0));
@@ -453,24 +522,63 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillParams p, int
     refresh_parts();
     // M(j): the products, then the operands of M(j+1) (each read after the
     // MFMAs that consume the registers it overwrites) and the copies
-    wait_vmcnt<6>();
+    wait_vmcnt<C::VMW>();
     bar();
     wait_lgkmcnt<0>();  // this wave's operands from M(j-1)
     // (the fences keep each operand read behind the MFMAs that consume the
     // registers it overwrites, so one register set per operand suffices)
-    if (kind == FULL || kind == LEADIN) gemm0(sc);
-    __builtin_amdgcn_sched_barrier(0);
-    read_k(kbuf(jr + 2));  // unused when slot j+2 is not computed
-    __builtin_amdgcn_sched_barrier(0);
-    if (kind == FULL || kind == LEADOUT) gemm1(pop);
-    __builtin_amdgcn_sched_barrier(0);
-    read_v(vrel(jr + 1));
-    copy_tile(vg, j + 5, vbuf(jr + 5));
-    copy_tile(kg, j + 6, kbuf(jr + 6));
+    if (kind == FULL) {
+      // Hand-ordered (each fence stops the scheduler from moving anything
+      // across): every MFMA is followed by the LDS read of the next slot's
+      // operand of the same index, into the registers the MFMA has just
+      // consumed, so the reads overlap the MFMAs.
+      const unsigned char* const kt = kbuf(jr + 2);
+      const unsigned char* const vt = vrel(jr + 1);
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[kb][e] = 0.f;
+#pragma unroll
+      for (int i = 0; i < C::NOP; ++i) {
+        const int kb = i / C::KS, s_ = i % C::KS;
+        sc[kb] = mfma_32x32x16(kreg[i], qreg[s_], sc[kb]);
+        __builtin_amdgcn_sched_barrier(0);
+        read_k_op(kt, i);
+        if (i == 1) copy_tile(vg, j + C::RING - 1, vbuf(jr + C::RING - 1));  // the copies ride early, in MFMA shadows
+        if (i == 2) copy_tile(kg, j + C::RING, kbuf(jr + C::RING));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < C::NOP; ++i) {
+        const int ps = i / C::DB, db = i % C::DB;
+        oacc[db] = mfma_32x32x16(vreg[i], pop[ps], oacc[db]);
+        __builtin_amdgcn_sched_barrier(0);
+        read_v_op(vt, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      if (kind == LEADIN) gemm0(sc);
+      __builtin_amdgcn_sched_barrier(0);
+      read_k(kbuf(jr + 2));  // unused when slot j+2 is not computed
+      __builtin_amdgcn_sched_barrier(0);
+      if (kind == LEADOUT) gemm1(pop);
+      __builtin_amdgcn_sched_barrier(0);
+      read_v(vrel(jr + 1));
+      copy_tile(vg, j + C::RING - 1, vbuf(jr + C::RING - 1));
+      copy_tile(kg, j + C::RING, kbuf(jr + C::RING));
+    }
     // X(j): the softmax of slot j+1
-    wait_vmcnt<6>();
+    wait_vmcnt<C::VMW>();
     bar();
-    if (kind == FULL || kind == LEADIN) {
+    if (kind == FULL) {
+      mask(j + 1, sc);
+      m_old = m_ref;
+      if (!keep_ref(sc)) move_ref(sc);
+      shift(sc);
+      rescale();
+      alu1(sc, pop);
+      pin_p();
+    } else if (kind == LEADIN) {
       mask(j + 1, sc);
       alu0(sc);
       rescale();
