@@ -26,6 +26,10 @@ headline prefill given an output gradient (TFLOP/s over 5 products of 2 d
 flops per visible pair, 2.5 times the forward count). "mla_decode" reports
 the absorbed multi-head latent attention decode (B=16, Hq=128, 576-wide latent
 rows, L ~ U[8192, 16384]) in GB/s over the latent rows read once.
+"configs" times the remaining single-GPU configurations on their own: the
+d=64 causal prefill (B=8, Hq=16, N=2048) at Hkv=16 and at Hkv=1 in TFLOP/s,
+and the batched decode (B=64, Hq=32, Hkv=8, d=128, 8192 tokens each) in
+GB/s, each with its roofline fraction.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -191,6 +195,68 @@ def chunked_report(dev, stream, steps: int) -> dict:
     }
 
 
+def c3_setup(dev, stream, hkv: int):
+    """The d=64 causal prefill (B=8, Hq=16, N=2048) with Hkv=16 (MHA) or 1 (MQA)."""
+    import torch
+    import exact_attention_flashattention_amd as pkg
+    from exact_attention_flashattention_amd import workloads as wl
+    x = wl.workload_3(hkv)
+    q, k, v = x.q.to(dev), x.k.to(dev), x.v.to(dev)
+    o = torch.empty_like(q)
+    fn = lambda: pkg.attn_prefill(q, k, v, o, scale=x.scale, stream=stream)
+    torch.cuda.synchronize()
+    return x, fn
+
+
+def c4_setup(dev, stream):
+    """The batched decode (B=64, Hq=32, Hkv=8, d=128, 8192 tokens each)."""
+    import torch
+    import exact_attention_flashattention_amd as pkg
+    from exact_attention_flashattention_amd import workloads as wl
+    x = wl.workload_4()
+    t = [a.to(dev) for a in (x.q, x.k_pages, x.v_pages, x.block_table, x.seq_lens)]
+    o = torch.empty_like(t[0])
+    splits = pkg.attn_decode_num_splits(x.B, x.Hkv, x.max_pages_per_seq, 0)
+    ws = torch.empty(pkg.attn_decode_workspace_size(x.B, x.Hq, x.Hkv, x.d, x.max_pages_per_seq, 0) // 4 + 4,
+                     dtype=torch.float32, device=dev)
+    fn = lambda: pkg.attn_decode(*t, o, scale=x.scale, num_splits=splits, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    return x, fn, splits
+
+
+def configs_report(dev, stream, steps: int) -> dict:
+    """The other single-GPU configurations, each timed on its own with HIP
+    events: the d=64 prefill at Hkv=16 and Hkv=1, and the batched decode."""
+    out = {}
+    for hkv in (16, 1):
+        x, fn = c3_setup(dev, stream, hkv)
+        t = time_calls(fn, stream, 3, steps)
+        fl = causal_flops(x.B, x.Hq, x.N, x.d)
+        tf = fl / (t * 1e-6) / 1e12
+        log(f"config 3 (Hkv={hkv}): prefill {t:.1f} us ({tf:.1f} TFLOP/s)")
+        out[f"prefill_d64_hkv{hkv}"] = {
+            "workload": x.name, "value": round(tf, 3), "unit": "TFLOP/s", "avg_launch_us": round(t, 2),
+            "flops_per_launch": fl,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                         "traffic": measured_traffic(f"prefill_d64_hkv{hkv}", PREFILL_SOURCES),
+                         "kernel": "prefill_bf16_kernel<64,8,64>"}}
+        del fn
+    x, fn, splits = c4_setup(dev, stream)
+    t = time_calls(fn, stream, 3, steps)
+    by = kv_bytes(x.seq_lens.tolist(), x.Hkv, x.d)
+    gb = by / (t * 1e-6) / 1e9
+    log(f"config 4: batched decode {t:.1f} us ({gb:.0f} GB/s)")
+    out["decode_batched"] = {
+        "workload": x.name, "value": round(gb, 2), "unit": "GB/s", "avg_call_us": round(t, 2),
+        "kv_bytes_per_call": by, "num_splits": splits,
+        "roofline": {"bound": "hbm", "achieved": round(gb, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gb / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("decode_batched", DECODE_SOURCES),
+                     "kernel": "decode_split_kernel<128> + decode_merge_kernel<128>"}}
+    return out
+
+
 def window_pairs(N: int, W: int, n_sink: int = 0) -> int:
     """Visible (query, key) pairs of causal self-attention with a window W
     and n_sink initial positions kept: row i sees min(i+1, W) window keys
@@ -325,7 +391,7 @@ def write_traffic(root: str) -> int:
 
     Expects <root>/<COUNTER>_<kind>/**/*counter_collection.csv for COUNTER in
     FETCH_SIZE, WRITE_SIZE and kind in prefill, decode, chunked, append,
-    backward, mla, copy,
+    backward, mla, c3_16, c3_1, c4, copy,
     as written by
         rocprofv3 --pmc <COUNTER> -d <root>/<COUNTER>_<kind> -o run --output-format csv \
             -- python bench.py --only <kind> --steps 3 --warmup 1 > <root>/<COUNTER>_<kind>.log
@@ -359,7 +425,11 @@ def write_traffic(root: str) -> int:
                                    ("kv_append", "append", ["kv_append_kernel"], APPEND_SOURCES),
                                    ("backward", "backward", ["bwd_pre_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"],
                                     BACKWARD_SOURCES),
-                                   ("decode_mla", "mla", ["mla_split_kernel", "mla_merge_kernel"], MLA_SOURCES)]:
+                                   ("decode_mla", "mla", ["mla_split_kernel", "mla_merge_kernel"], MLA_SOURCES),
+                                   ("prefill_d64_hkv16", "c3_16", ["prefill_bf16_kernel"], PREFILL_SOURCES),
+                                   ("prefill_d64_hkv1", "c3_1", ["prefill_bf16_kernel"], PREFILL_SOURCES),
+                                   ("decode_batched", "c4", ["decode_split_kernel", "decode_merge_kernel"],
+                                    DECODE_SOURCES)]:
         for counter in ("FETCH_SIZE", "WRITE_SIZE"):
             ran = None
             with open(os.path.join(root, f"{counter}_{kind}.log")) as f:
@@ -390,6 +460,12 @@ def only(args, dev) -> int:
         o = torch.empty_like(q)
         fn = lambda: pkg.attn_prefill(q, k, v, o, scale=x.scale, stream=stream)
         work = {"flops_per_launch": causal_flops(x.B, x.Hq, x.N, x.d)}
+    elif args.only in ("c3_16", "c3_1"):
+        x, fn = c3_setup(dev, stream, 16 if args.only == "c3_16" else 1)
+        work = {"flops_per_launch": causal_flops(x.B, x.Hq, x.N, x.d)}
+    elif args.only == "c4":
+        x, fn, _ = c4_setup(dev, stream)
+        work = {"kv_bytes_per_call": kv_bytes(x.seq_lens.tolist(), x.Hkv, x.d)}
     elif args.only == "mla":
         x, fn = mla_setup(dev, stream)
         work = {"kv_bytes_per_call": int(x.seq_lens.sum()) * (x.d_c + x.d_r) * 2}
@@ -426,7 +502,8 @@ def only(args, dev) -> int:
     b.record(stream)
     torch.cuda.synchronize()
     srcs = {"prefill": PREFILL_SOURCES, "decode": DECODE_SOURCES, "chunked": PREFILL_SOURCES,
-            "append": APPEND_SOURCES, "backward": BACKWARD_SOURCES, "mla": MLA_SOURCES}.get(args.only)
+            "append": APPEND_SOURCES, "backward": BACKWARD_SOURCES, "mla": MLA_SOURCES,
+            "c3_16": PREFILL_SOURCES, "c3_1": PREFILL_SOURCES, "c4": DECODE_SOURCES}.get(args.only)
     print(json.dumps({"only": args.only, "steps": args.steps,
                       "avg_us": round(a.elapsed_time(b) * 1e3 / args.steps, 2),
                       "source_sha256": source_hash(*srcs) if srcs else None, **work}), flush=True)
@@ -443,7 +520,8 @@ def main() -> int:
                     help="skip the chunked-prefill (KV append + paged prefill) and variant reports")
     ap.add_argument("--cpu-batches", type=int, default=2,
                     help="batch entries of the headline prefill the CPU oracle is timed on")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy", "chunked", "append", "backward", "mla"],
+    ap.add_argument("--only", choices=["prefill", "decode", "copy", "chunked", "append", "backward", "mla",
+                                       "c3_16", "c3_1", "c4"],
                     default=None,
                     help="launch only this kernel (for counter runs under rocprofv3); "
                          "'copy' is a plain 1 GiB device copy used to calibrate byte counters")
@@ -563,6 +641,7 @@ def main() -> int:
         "variants": None,
         "backward": None,
         "mla_decode": None,
+        "configs": None,
         "cpu_baseline": None,
     }
     if not args.no_chunked:
@@ -570,6 +649,7 @@ def main() -> int:
         result["variants"] = variants_report(dev, stream, max(10, args.steps // 2))
         result["backward"] = backward_report(dev, stream, max(10, args.steps // 5))
         result["mla_decode"] = mla_report(dev, stream, max(10, args.steps // 2))
+    result["configs"] = configs_report(dev, stream, max(10, args.steps // 2))
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(x2, x5, args.cpu_batches)

@@ -191,7 +191,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
   // A learned sink logit s_h is an extra score column with zero value: it
   // enters as the initial state m = s_h, l = e^0 = 1, O = 0.
-  float m_ref = kNegInf, l_run = 0.f;
+  // m_ref starts at the most negative finite float ("no key yet"): masked
+  // scores stay -inf through s*c2 - m_ref, so no -inf guards are needed, and
+  // the first finite row max always moves it (the rescale factor is then 0).
+  float m_ref = -3.402823466e38f, l_run = 0.f;
   if (p.sinks) {
     m_ref = p.sinks[h] * 1.4426950408889634f;  // base-2 units, like the scores
     l_run = h2 == 0 ? 1.f : 0.f;  // the two lane halves' sums are added at the end
@@ -384,18 +387,20 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
           s[kb][e] = (off > lim || (off < lo && off >= sk)) ? kNegInf : s[kb][e];
         }
     }
-    // row max over four interleaved running maxima (one running max would be
-    // a single chain of dependent v_max3 on the critical path of every tile)
+    // max of this lane's keys over four interleaved running maxima (one
+    // running max would be a single chain of dependent v_max3 on the critical
+    // path of every tile); a row's max exceeds the reference by more than the
+    // threshold iff one of its two lane halves does, so the cross-lane row max
+    // is taken only on the rare tiles that move the reference
     float rm[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) rm[e & 3] = fmaxf(rm[e & 3], s[kb][e]);
-    const float mr = halves_max(fmaxf(fmaxf(rm[0], rm[1]), fmaxf(rm[2], rm[3])));
-    const float mt = (mr == kNegInf) ? kNegInf : mr * c2;
-    if (__builtin_amdgcn_ballot_w64(mt > m_ref + kRescaleTau)) {
-      const float m_new = fmaxf(m_ref, mt);
-      const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+    const float mh = fmaxf(fmaxf(rm[0], rm[1]), fmaxf(rm[2], rm[3]));
+    if (__builtin_amdgcn_ballot_w64(mh * c2 > m_ref + kRescaleTau)) {
+      const float m_new = fmaxf(m_ref, halves_max(mh) * c2);
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
       m_ref = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -406,7 +411,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillParams 
   };
   // P = 2^(s - m) rounded to bf16, l += rowsum(P), O^T += V^T P^T for tile t
   auto pv = [&](const unsigned char* __restrict__ vt_lds, const f32x16_t (&s)[C::KB]) __attribute__((always_inline)) {  // V tile of tile j
-    const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
+    const float neg_m = -m_ref;
     u32x4_t pop[C::PS];
     float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
