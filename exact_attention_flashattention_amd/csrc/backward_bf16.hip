@@ -165,8 +165,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams p, int n
     ld_off[u] = (unsigned)row * row_bytes + (unsigned)(ld_pos ^ swz<C::CPR>(row)) * 16u;
   }
   constexpr int kLoads = 2 * C::IPW + 1;  // Q and dO pieces, plus the stats copy
-  auto issue = [&](int slot, unsigned char* __restrict__ bq, unsigned char* __restrict__ bd,
-                   unsigned char* __restrict__ bs) __attribute__((always_inline)) {
+  auto issue = [&](int slot) __attribute__((always_inline)) {
     const int hg = slot / nT, t = T - 1 - (slot - hg * nT);
     const int h = kvh * g + hg;
     const int r0 = t * BN;
@@ -182,14 +181,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams p, int n
         const int row = i * C::RPI + ld_row;
         off = (unsigned)(min(r0 + row, N - 1) - r0) * row_bytes + (unsigned)(ld_pos ^ swz<C::CPR>(row)) * 16u;
       }
-      load_to_lds(qt + off, bq + i * 1024);
-      load_to_lds(dt + off, bd + i * 1024);
+      load_to_lds(qt + off, qbuf(slot) + i * 1024);
+      load_to_lds(dt + off, dbuf(slot) + i * 1024);
     }
     // stats rows r0 .. r0+63 (padded arrays): lanes 0-15 lse2, 16-31 D, 32-63 again
     const long long srow = ((long long)b * p.Hq + h) * p.Npad + r0;
     const int l32 = lane & 31;
     const float* src = (l32 < 16 ? p.lse2 : p.dvec) + srow + (l32 & 15) * 4;
-    load_to_lds(src, bs);
+    load_to_lds(src, sbuf(slot));
   };
   auto wait_tiles_after = [&](int n) __attribute__((always_inline)) {  // all but the n newest slots landed
     if (n >= 2)
@@ -230,10 +229,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams p, int n
   };
 
   // one streamed slot: the query tile's contribution to this wave's dK, dV
-  auto compute = [&](int slot, const unsigned char* __restrict__ qt, const unsigned char* __restrict__ dt,
-                     const unsigned char* __restrict__ st) __attribute__((always_inline)) {
+  auto compute = [&](int slot) __attribute__((always_inline)) {
     const int hg = slot / nT, t = T - 1 - (slot - hg * nT);
     const int r0 = t * BN;
+    const unsigned char* qt = qbuf(slot);
+    const unsigned char* dt = dbuf(slot);
+    const unsigned char* st = sbuf(slot);
     const bool need_mask = (p.causal && r0 < kw0 + 31) || (r0 + BN > N) || (kw0 + 31 >= N);
 #pragma unroll
     for (int rb = 0; rb < C::RB; ++rb) {
@@ -299,29 +300,19 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams p, int n
   };
 
   // ---- the stream: issue slot j+3 at the top of iteration j (into the buffer
-  // of slot j-1); slot j+1 must have landed before the barrier ending j.
-  // Each wave waits for its own copies (vmcnt) and its own reads of the
-  // buffer the next copy overwrites (lgkmcnt) before the barrier; the buffers
-  // reach the step as distinct restrict pointers, so reading slot j does not
-  // wait for the copy into slot j+3 either.
-  if (n_slots > 0) issue(0, qbuf(0), dbuf(0), sbuf(0));
-  if (n_slots > 1) issue(1, qbuf(1), dbuf(1), sbuf(1));
-  if (n_slots > 2) issue(2, qbuf(2), dbuf(2), sbuf(2));
+  // of slot j-1); slot j+1 must have landed before the barrier ending j
+  if (n_slots > 0) issue(0);
+  if (n_slots > 1) issue(1);
+  if (n_slots > 2) issue(2);
   wait_tiles_after(min(n_slots - 1, 2));
-  barrier_nofence();
-  auto step = [&](int j, unsigned char* __restrict__ iq, unsigned char* __restrict__ id,
-                  unsigned char* __restrict__ is, const unsigned char* __restrict__ rq,
-                  const unsigned char* __restrict__ rd, const unsigned char* __restrict__ rs)
-      __attribute__((always_inline)) {
-    if (j + 3 < n_slots) issue(j + 3, iq, id, is);
+  __syncthreads();
+  for (int j = 0; j < n_slots; ++j) {
+    if (j + 3 < n_slots) issue(j + 3);
     const int r = j % nT;
-    if (wave_live && r <= nT - 1 - w_t0) compute(j, rq, rd, rs);
+    if (wave_live && r <= nT - 1 - w_t0) compute(j);
     wait_tiles_after(min(n_slots - j - 2, 2));
-    wait_lgkmcnt<0>();
-    barrier_nofence();
-  };
-  for (int j = 0; j < n_slots; ++j)
-    step(j, qbuf(j + 3), dbuf(j + 3), sbuf(j + 3), qbuf(j), dbuf(j), sbuf(j));
+    __syncthreads();
+  }
 
   // ---- epilogue: dK = scale dK^T, dV = dV^T, bf16 rows through LDS ----------------
   unsigned char* const ost = lds + wave * 32 * C::OROW;
@@ -418,7 +409,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p, int n_q
     ld_off[u] = (unsigned)row * row_bytes + (unsigned)(ld_pos ^ swz<C::CPR>(row)) * 16u;
   }
   constexpr int kLoads = 2 * C::IPW;
-  auto issue = [&](int t, unsigned char* __restrict__ bk, unsigned char* __restrict__ bv) __attribute__((always_inline)) {
+  auto issue = [&](int t) __attribute__((always_inline)) {
     const int k0 = t * BN;
     const char* kt = (const char*)((const __bf16*)p.k + b * p.k_sb + kvh * p.k_sh) + (long long)k0 * row_bytes;
     const char* vt = (const char*)((const __bf16*)p.v + b * p.k_sb + kvh * p.k_sh) + (long long)k0 * row_bytes;
@@ -432,8 +423,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p, int n_q
         const int row = i * C::RPI + ld_row;
         off = (unsigned)(min(k0 + row, N - 1) - k0) * row_bytes + (unsigned)(ld_pos ^ swz<C::CPR>(row)) * 16u;
       }
-      load_to_lds(kt + off, bk + i * 1024);
-      load_to_lds(vt + off, bv + i * 1024);
+      load_to_lds(kt + off, kbuf(t) + i * 1024);
+      load_to_lds(vt + off, vbuf(t) + i * 1024);
     }
   };
   auto wait_tiles_after = [&](int n) __attribute__((always_inline)) {
@@ -473,9 +464,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p, int n_q
     return a;
   };
 
-  auto compute = [&](int t, const unsigned char* __restrict__ kt, const unsigned char* __restrict__ vt)
-      __attribute__((always_inline)) {
+  auto compute = [&](int t) __attribute__((always_inline)) {
     const int k0 = t * BN;
+    const unsigned char* kt = kbuf(t);
+    const unsigned char* vt = vbuf(t);
     const bool need_mask = (p.causal && k0 + BN - 1 > qw0) || (k0 + BN > N);
 #pragma unroll
     for (int kb = 0; kb < C::RB; ++kb) {
@@ -521,22 +513,17 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p, int n_q
     }
   };
 
-  // the stream as in the dK/dV kernel: explicit waits, restrict buffers
-  if (n_tiles > 0) issue(0, kbuf(0), vbuf(0));
-  if (n_tiles > 1) issue(1, kbuf(1), vbuf(1));
-  if (n_tiles > 2) issue(2, kbuf(2), vbuf(2));
+  if (n_tiles > 0) issue(0);
+  if (n_tiles > 1) issue(1);
+  if (n_tiles > 2) issue(2);
   wait_tiles_after(min(n_tiles - 1, 2));
-  barrier_nofence();
-  auto step = [&](int j, unsigned char* __restrict__ ik, unsigned char* __restrict__ iv,
-                  const unsigned char* __restrict__ rk, const unsigned char* __restrict__ rv)
-      __attribute__((always_inline)) {
-    if (j + 3 < n_tiles) issue(j + 3, ik, iv);
-    if (j < wave_tiles) compute(j, rk, rv);
+  __syncthreads();
+  for (int j = 0; j < n_tiles; ++j) {
+    if (j + 3 < n_tiles) issue(j + 3);
+    if (j < wave_tiles) compute(j);
     wait_tiles_after(min(n_tiles - j - 2, 2));
-    wait_lgkmcnt<0>();
-    barrier_nofence();
-  };
-  for (int j = 0; j < n_tiles; ++j) step(j, kbuf(j + 3), vbuf(j + 3), kbuf(j), vbuf(j));
+    __syncthreads();
+  }
 
   // ---- epilogue: dQ = scale dQ^T, bf16 rows through LDS ---------------------------
   unsigned char* const ost = lds + wave * 32 * C::OROW;

@@ -88,35 +88,6 @@ __global__ __launch_bounds__(NWM * 64, 1) void mla_split_kernel(MlaParams p, int
   const int n_steps = (pg_end - pg_begin + 1) / 2;
   const int32_t* __restrict__ table = p.block_table + (long long)b * p.max_pages_per_seq;
   const unsigned char* __restrict__ pool = (const unsigned char*)p.kv_pages;
-  // The split's page numbers, read once: lane i holds entries pg_begin + i
-  // and pg_begin + 64 + i. A vector load of the table inside the loop would
-  // need a vmcnt wait, which would also wait for every copy in flight; a
-  // split of more than 128 pages reads its entries with scalar loads.
-  const int tab_n = pg_end - pg_begin;
-  const bool tab_regs = tab_n <= 128;
-  int tab_lo = 0, tab_hi = 0, page_last = 0;
-  if (np > 0) {
-    page_last = table[np - 1];
-    if (tab_regs) {
-      if (lane < tab_n) tab_lo = table[pg_begin + lane];
-      if (64 + lane < tab_n) tab_hi = table[pg_begin + 64 + lane];
-    }
-  }
-  // consume the entries here, before any copy is in flight, so that the
-  // wait for these loads is not placed inside the loop
-  asm volatile("" : "+v"(tab_lo), "+v"(tab_hi), "+v"(page_last));
-  page_last = __builtin_amdgcn_readfirstlane(page_last);
-  auto page_at = [&](int pg) __attribute__((always_inline)) {  // pg in [pg_begin, pg_end)
-    int v;
-    if (tab_regs) {
-      const int i = pg - pg_begin;
-      v = i < 64 ? __builtin_amdgcn_readlane(tab_lo, i) : __builtin_amdgcn_readlane(tab_hi, i - 64);
-    } else {
-      const int32_t* e = table + pg;  // uniform address
-      asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(e) : "memory");
-    }
-    return v;
-  };
 
   // q of this lane's head as the B operand (k-step ks: dims ks*32 + grp*8 .. +7)
   u32x4_t qreg[KS];
@@ -134,11 +105,13 @@ __global__ __launch_bounds__(NWM * 64, 1) void mla_split_kernel(MlaParams p, int
   // (chunks 72 and 73 are the row's padding; slots past the 32 rows are spare). A row
   // past the end of the sequence, or the missing second page of the last
   // step, is loaded from the sequence's last token.
-  auto issue = [&](int step, unsigned char* __restrict__ buf) __attribute__((always_inline)) {
+  auto issue = [&](int step) __attribute__((always_inline)) {
     const int pa = pg_begin + 2 * step, pb = pa + 1;
-    const int page_a = page_at(pa);
-    const int page_b = pb < pg_end ? page_at(pb) : page_a;
+    const int page_a = table[pa];
+    const int page_b = pb < pg_end ? table[pb] : page_a;
+    const int page_last = table[np - 1];
     const int t_last = L - 1;
+    unsigned char* const buf = lds + (step % NBUF_M) * STEP_BYTES;
 #pragma unroll
     for (int u = 0; u < IPW_M; ++u) {
       const int i = wave + u * NWM;
@@ -168,7 +141,8 @@ __global__ __launch_bounds__(NWM * 64, 1) void mla_split_kernel(MlaParams p, int
     for (int r = 0; r < 2; ++r) tpart[r] = (unsigned)((r * 16 + 4 * grp + tt) * ROWP + tu * 8);
   }
 
-  auto compute = [&](int step, const unsigned char* __restrict__ kt) __attribute__((always_inline)) {
+  auto compute = [&](int step) __attribute__((always_inline)) {
+    const unsigned char* kt = lds + (step % NBUF_M) * STEP_BYTES;
     const int pa = pg_begin + 2 * step, pb = pa + 1;
     // S^T for tokens [pa*16, +16) (block 0) and [pb*16, +16) (block 1)
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -232,26 +206,17 @@ __global__ __launch_bounds__(NWM * 64, 1) void mla_split_kernel(MlaParams p, int
     else
       wait_vmcnt<0>();
   };
-  // Each wave waits for its own copies (vmcnt) and its own reads of the buffer
-  // the next copy overwrites (lgkmcnt) before each barrier; __syncthreads()
-  // would also wait for the copies of the steps still ahead. The buffers
-  // reach a step as distinct restrict pointers, so reading step j does not
-  // wait for the copy into step j+3 either.
-  auto buf = [&](int step) __attribute__((always_inline)) { return lds + (step % NBUF_M) * STEP_BYTES; };
-  if (n_steps > 0) issue(0, buf(0));
-  if (n_steps > 1) issue(1, buf(1));
-  if (n_steps > 2) issue(2, buf(2));
+  if (n_steps > 0) issue(0);
+  if (n_steps > 1) issue(1);
+  if (n_steps > 2) issue(2);
   wait_after(min(n_steps - 1, 2));
-  barrier_nofence();
-  auto step_j = [&](int j, unsigned char* __restrict__ b_issue, const unsigned char* __restrict__ b_read)
-      __attribute__((always_inline)) {
-    if (j + 3 < n_steps) issue(j + 3, b_issue);
-    if (wave_live) compute(j, b_read);
+  __syncthreads();
+  for (int j = 0; j < n_steps; ++j) {
+    if (j + 3 < n_steps) issue(j + 3);
+    if (wave_live) compute(j);
     wait_after(min(n_steps - j - 2, 2));
-    wait_lgkmcnt<0>();
-    barrier_nofence();
-  };
-  for (int j = 0; j < n_steps; ++j) step_j(j, buf(j + 3), buf(j));
+    __syncthreads();
+  }
 
   // the four lane groups each summed their own tokens
   l_run += __shfl_xor(l_run, 16);
