@@ -240,7 +240,7 @@ def configs_report(dev, stream, steps: int) -> dict:
             "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / BF16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic(f"prefill_d64_hkv{hkv}", PREFILL_SOURCES),
-                         "kernel": "prefill_bf16_kernel<64,8,64>"}}
+                         "kernel": "prefill_bf16_kernel<64,8,32>"}}
         del fn
     x, fn, splits = c4_setup(dev, stream)
     t = time_calls(fn, stream, 3, steps)
