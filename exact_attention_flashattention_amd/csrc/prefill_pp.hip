@@ -35,11 +35,11 @@
 //    k-step takes the keys in that order), V^T read from LDS with
 //    ds_read_b64_tr_b16 (four consecutive keys of one dimension per lane).
 //  * K and V tiles go HBM -> LDS with global_load_lds_dwordx4 into rings of
-//    six buffers each, every 16-byte chunk at a row-swizzled position so the
-//    K operand reads and the transposed V reads are free of bank conflicts.
-//    Copies run five and six slots ahead; each wave waits for its own copies
-//    with an explicit vmcnt count before each barrier (__syncthreads() would
-//    wait for every copy in flight).
+//    R buffers each (R = 6 by default), every 16-byte chunk at a row-swizzled
+//    position so the K operand reads and the transposed V reads are free of
+//    bank conflicts. V copies run R-1 slots ahead and K copies R; each wave
+//    waits for its own copies with an explicit vmcnt count before each
+//    barrier (__syncthreads() would wait for every copy in flight).
 //  * The reference point m of 2^(s - m) moves only when a row's max exceeds it
 //    by more than 2^8 (then O and l are rescaled exactly), so the accumulators
 //    are untouched on most slots; the weights stay below 2^8.
@@ -505,18 +505,19 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillParams p, int
   // group 0 (it opens with an empty phase, group 0 closes with one), so the
   // matrix phase of one wave of a SIMD meets the vector phase of the other.
   //   M(j): S_{j+1} = K_{j+1} Q^T and O += V_j P_j; then the K_{j+2} and
-  //         V_{j+1} operands from LDS and the copies V_{j+5}, K_{j+6}
+  //         V_{j+1} operands from LDS and the copies V_{j+R-1}, K_{j+R}
   //   X(j): mask, row max, exponentials and row sums of slot j+1
   // A wave issues at most one instruction every few cycles, so the data
   // movement rides in the matrix phase (between MFMAs a wave is idle) and
   // the vector phase holds only the softmax.
-  // Copies: six buffers per ring. Slot t's K and V are read in M(t-2) and
+  // Copies: R buffers per ring. Slot t's K and V are read in M(t-2) and
   // M(t-1); their buffers are rewritten only from M(t) and M(t+1) on, after
   // the barriers that follow the waits for those reads (each wave waits for
   // its LDS reads at the start of its next matrix phase). Before every
-  // barrier each wave waits until at most six of its copies are in flight,
-  // which completes the copies of slot j+2's K and j+1's V (issued in M(j-4)
-  // by both groups) before the barrier that opens M(j) of group 0.
+  // barrier each wave waits until at most 2(R-3) of its copies are in flight
+  // (those of its last R-3 matrix phases), which completes the copies of slot
+  // j+2's K and j+1's V (issued in M(j+2-R) by both groups) before the
+  // barrier that opens M(j) of group 0.
   constexpr int IDLE = 0, LEADIN = 1, FULL = 2, LEADOUT = 3;
   auto iteration = [&](int j, int jr, int kind) __attribute__((always_inline)) {
     refresh_parts();
@@ -594,7 +595,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillParams p, int
   if (gf > 0 && gf < ge) step(j++, LEADIN);
   // j == gf here when the group has work: slots j and j+1 both computed
   for (; j % C::RING && j + 1 < ge; ++j) step(j, FULL);
-  // six slots per trip: ring positions are compile-time constants
+  // R slots per trip: ring positions are compile-time constants
   for (; j + C::RING < ge; j += C::RING) {
 #pragma unroll
     for (int u = 0; u < C::RING; ++u) iteration(j + u, u, FULL);
