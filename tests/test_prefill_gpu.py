@@ -171,3 +171,23 @@ def test_workload_2_full_size():
 @pytest.mark.parametrize("hkv", [16, 1])
 def test_workload_3_full_size(hkv):
     full_size_check(wl.workload_3(hkv))
+
+
+@pytest.mark.parametrize("d,Hkv,causal", [(128, 1, True), (64, 2, True), (128, 2, False)])
+def test_long_sequence_sampled_rows(d, Hkv, causal):
+    """A 32768-token sequence (128 query tiles, 512 or 1024 key tiles per
+    work-group): rows at tile edges and at the far end, every head, against
+    the oracle's rows. Exercises the longest loops and the largest offsets of
+    a single sequence."""
+    N, Hq = 32768, 4
+    x = wl.prefill_inputs(1, N, Hq, Hkv, d, seed=1500 + d + Hkv, causal=causal)
+    log(f"case: bf16 B=1 N={N} Hq={Hq} Hkv={Hkv} d={d} causal={causal}")
+    got, _ = run(x)
+    assert bool(torch.isfinite(got.float()).all())
+    rows = [0, 1, 31, 32, 255, 256, 4095, 16384, 32766, 32767]
+    samples = [(0, i, h) for h in range(Hq) for i in rows]
+    ref = ao.prefill_rows_ref(x.q, x.k, x.v, x.scale, samples, causal=causal)
+    g = np.stack([got[0, i, h].double().numpy() for (_, i, h) in samples])
+    e = np.abs(g - ref)
+    log(f"  {len(samples)} rows: max-abs {e.max():.3e} mean-abs {e.mean():.3e}")
+    assert e.max() <= BF16_MAX and e.mean() <= BF16_MEAN
