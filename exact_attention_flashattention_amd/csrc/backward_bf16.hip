@@ -11,13 +11,14 @@
 //
 // Three kernels:
 //  * bwd_pre: D_i and lse2_i = lse_i * log2(e) per row, into the workspace.
-//  * bwd_dkdv: a work-group owns 32 keys per wave of one (b, KV head) and
-//    streams the Q and dO tiles (and their D, lse2) of every query head of the
-//    group through LDS; dK^T and dV^T stay in registers, so no atomics.
+//  * bwd_dkdv: a work-group owns 128 keys of one (b, KV head), 32 per pair
+//    of waves, and streams the Q and dO tiles (and their D, lse2) of every
+//    query head of the group through LDS; one wave of a pair keeps dV^T and
+//    the other dK^T in registers, so no atomics.
 //  * bwd_dq: a work-group owns 32 queries per wave of one (b, h) and streams
 //    the K and V tiles, like the forward.
-// Both main kernels copy tiles HBM -> LDS with global_load_lds into a ring of
-// four buffers (one barrier per tile) and read them with the same XOR swizzle
+// Both main kernels copy tiles HBM -> LDS with global_load_lds into a ring
+// (one barrier per tile) and read them with the same XOR swizzle
 // as the forward: row reads for the A operand of S = Q K^T / dP = dO V^T and
 // ds_read_b64_tr_b16 transposed reads for the A operand of the dK, dV, dQ
 // products. Score tiles are held in the MFMA accumulator layout whose lanes
@@ -94,16 +95,33 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK and dV. Work item = (KV head, b, key block of 32*NW keys); the streamed
+// dK and dV. Work item = (KV head, b, key block of 32*NP keys); the streamed
 // slots are (query head of the group, query tile) with the tiles that hold a
 // query at or after the block's first key (causal) or all tiles.
-template <int D, int NW, int BN>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
+//
+// The work of a 32-key block is split over a pair of waves that share a SIMD
+// (waves w and w + NP): the "P wave" w computes S = Q K^T, the weights
+// P = 2^(S c2 - lse2) and dV^T += dO^T P, and hands P (bf16) to its partner
+// through LDS; the "dS wave" w + NP computes dP = dO V^T, dS = P (dP - D) and
+// dK^T += Q^T dS. The dS wave runs one slot behind: in slot j it finishes
+// slot j - 1 (whose P was written during slot j - 1) and then forms dP for
+// slot j, which it keeps in registers. Each wave holds one of K, V and one of
+// the two gradients, so two waves fit on a SIMD, and the exponentials of one
+// wave overlap the products of the other.
+template <int D, int NP, int BN>
+__global__ __launch_bounds__(2 * NP * 64, 1) void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
+  constexpr int NW = 2 * NP;
   using C = BCfg<D, NW, BN>;
-  constexpr int SREG = 2 * C::BREG;              // per-wave copies of (lse2, D) rows
-  constexpr int SBUF = NW * 1024;                // one buffer's stats: a 1 KiB copy per wave
-  constexpr int LDS_MAIN = SREG + C::NBUF * SBUF;
+  constexpr int NB = 3;                          // ring: slot j-1 (dS wave), j (both), j+1 (landing)
+  constexpr int RING = NB * C::TILE;             // Q tiles at [0, RING), dO tiles at [RING, 2 RING)
+  constexpr int SREG = 2 * RING;                 // per-wave copies of (lse2, D) rows
+  constexpr int SBUF = NW * 1024;
+  constexpr int PREG = SREG + NB * SBUF;         // P hand-over: 2 slots x NP pairs x RB blocks x 2 KiB
+  constexpr int PPAIR = C::RB * 2 * 1024;
+  constexpr int PSLOT = NP * PPAIR;
+  constexpr int LDS_MAIN = PREG + 2 * PSLOT;
   constexpr int LDS_OUT = NW * 32 * C::OROW;
+  static_assert(LDS_MAIN <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_MAIN > LDS_OUT ? LDS_MAIN : LDS_OUT];
 
   const int g = p.Hq / p.Hkv;
@@ -115,46 +133,61 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams p, int n
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pi = wave % NP;                    // key block of the wave pair
+  const bool ds_wave = wave >= NP;
   const int c = lane & 31, h2 = lane >> 5;
-  const int k_blk0 = kblk * NW * 32;
-  const int kw0 = k_blk0 + wave * 32;  // this wave's first key
-  const int kj = kw0 + c;              // this lane's key (column of S)
+  const int k_blk0 = kblk * NP * 32;
+  const int kw0 = k_blk0 + pi * 32;            // the pair's first key
+  const int kj = kw0 + c;                      // this lane's key (column of S)
   const float c2 = p.scale_log2;
 
-  // K and V of this lane's key as B operands (k-step s: dims s*16 + h2*8 .. +7)
-  u32x4_t kreg[C::KS], vreg[C::KS];
+  // K (P wave) or V (dS wave) of this lane's key as B operands (k-step s:
+  // dims s*16 + h2*8 .. +7)
+  u32x4_t kvreg[C::KS];
   {
     const int kc = min(kj, N - 1);
-    const __bf16* kg = (const __bf16*)p.k + b * p.k_sb + (long long)kc * p.k_sn + kvh * p.k_sh;
-    const __bf16* vg = (const __bf16*)p.v + b * p.k_sb + (long long)kc * p.k_sn + kvh * p.k_sh;
+    const __bf16* src = (const __bf16*)(ds_wave ? p.v : p.k) + b * p.k_sb + (long long)kc * p.k_sn + kvh * p.k_sh;
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) {
-      kreg[s] = *(const u32x4_t*)(kg + s * 16 + h2 * 8);
-      vreg[s] = *(const u32x4_t*)(vg + s * 16 + h2 * 8);
-    }
+    for (int s = 0; s < C::KS; ++s) kvreg[s] = *(const u32x4_t*)(src + s * 16 + h2 * 8);
   }
-  f32x16_t dk[C::DB], dv[C::DB];
+  f32x16_t grad[C::DB];  // dV^T (P wave) or dK^T / scale (dS wave)
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) dk[db][e] = dv[db][e] = 0.f;
+    for (int e = 0; e < 16; ++e) grad[db][e] = 0.f;
+  f32x16_t dp[C::RB];  // dS wave: dP of the current slot, carried into the next
+#pragma unroll
+  for (int rb = 0; rb < C::RB; ++rb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dp[rb][e] = 0.f;
 
   // streamed slots: (query head hg, query tile T - 1 - r). The tiles of a
-  // head run from the last one down to the block's first: the work-groups of
-  // one (b, KV head) run side by side, and all of them start on the same last
-  // tile, so they read the same Q/dO tiles at about the same time and L2
-  // serves most of them (HBM reads of this kernel 1.67 GB -> 0.75 GB on the
-  // headline backward; ascending order had each group start on its own tile).
+  // head run from the last one down to the block's first, so the work-groups
+  // of one (b, KV head), which run side by side, start on the same last tile
+  // and L2 serves most of their Q/dO reads.
   const int T = (N + BN - 1) / BN;
   const int t0 = p.causal ? k_blk0 / BN : 0;
   const int nT = T - t0;
   const int n_slots = g * nT;
-  const int w_t0 = (p.causal ? kw0 / BN : 0) - t0;  // this wave's first tile within a head's run
-  const bool wave_live = kw0 < N;
+  const int w_t0 = (p.causal ? kw0 / BN : 0) - t0;  // the pair's first tile within a head's run
+  const bool pair_live = kw0 < N;
+  auto live = [&](int slot) __attribute__((always_inline)) {
+    return pair_live && (slot % nT) <= nT - 1 - w_t0;
+  };
 
-  auto qbuf = [&](int s) __attribute__((always_inline)) { return lds + (s % C::NBUF) * C::TILE; };
-  auto dbuf = [&](int s) __attribute__((always_inline)) { return lds + C::BREG + (s % C::NBUF) * C::TILE; };
-  auto sbuf = [&](int s) __attribute__((always_inline)) { return lds + SREG + (s % C::NBUF) * SBUF + wave * 1024; };
+  // Buffer addresses of a slot. The offset goes through an empty asm
+  // statement so that it is formed once per slot in a scalar register: left
+  // to itself the compiler precomputes every (buffer, lane offset) sum as a
+  // loop-invariant vector register (most exceed the 16-bit immediate offset
+  // of the LDS instructions) and runs out of registers.
+  auto at = [&](unsigned off) __attribute__((always_inline)) {
+    asm volatile("" : "+s"(off));
+    return lds + off;
+  };
+  auto qbuf = [&](int s) __attribute__((always_inline)) { return at((unsigned)(s % NB) * C::TILE); };
+  auto dbuf = [&](int s) __attribute__((always_inline)) { return at(RING + (unsigned)(s % NB) * C::TILE); };
+  auto sbuf = [&](int s) __attribute__((always_inline)) { return at(SREG + (unsigned)(s % NB) * SBUF + wave * 1024); };
+  auto pbuf = [&](int s) __attribute__((always_inline)) { return at(PREG + (unsigned)(s & 1) * PSLOT + pi * PPAIR); };
 
   const int ld_row = lane / C::CPR, ld_pos = lane % C::CPR;
   const unsigned row_bytes = (unsigned)p.q_sn * 2u;
@@ -164,7 +197,6 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams p, int n
     const int row = (wave + u * NW) * C::RPI + ld_row;
     ld_off[u] = (unsigned)row * row_bytes + (unsigned)(ld_pos ^ swz<C::CPR>(row)) * 16u;
   }
-  constexpr int kLoads = 2 * C::IPW + 1;  // Q and dO pieces, plus the stats copy
   auto issue = [&](int slot) __attribute__((always_inline)) {
     const int hg = slot / nT, t = T - 1 - (slot - hg * nT);
     const int h = kvh * g + hg;
@@ -189,14 +221,6 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams p, int n
     const int l32 = lane & 31;
     const float* src = (l32 < 16 ? p.lse2 : p.dvec) + srow + (l32 & 15) * 4;
     load_to_lds(src, sbuf(slot));
-  };
-  auto wait_tiles_after = [&](int n) __attribute__((always_inline)) {  // all but the n newest slots landed
-    if (n >= 2)
-      wait_vmcnt<2 * kLoads>();
-    else if (n == 1)
-      wait_vmcnt<kLoads>();
-    else
-      wait_vmcnt<0>();
   };
 
   // per-lane parts of the LDS reads (bytes from a tile's start)
@@ -227,119 +251,151 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams p, int n
     }
     return a;
   };
+  // 32 rows of a streamed tile times this pair's 32 keys: lane (key c) holds
+  // query rows rb*32 + 8 (e/4) + 4 h2 + e%4
+  auto row_product = [&](const unsigned char* tile, int rb) __attribute__((always_inline)) {
+    f32x16_t acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s)
+      acc = mfma_32x32x16(*(const u32x4_t*)(tile + rpart[s] + rb * 32 * C::ROWB), kvreg[s], acc);
+    return acc;
+  };
+  // P and dS words, in the accumulator's lane layout: k-step ps = 2 rb + kk
+  // holds the rows of groups r = 2 kk, 2 kk + 1 (words 2(r&1), 2(r&1)+1), so
+  // the packed words are the B operand of the transposed products as they are
+  const int hand = lane * 16;  // byte offset of this lane's 16 bytes in a 1 KiB hand-over block
 
-  // one streamed slot: the query tile's contribution to this wave's dK, dV
-  auto compute = [&](int slot) __attribute__((always_inline)) {
-    const int hg = slot / nT, t = T - 1 - (slot - hg * nT);
+  // P wave, slot j: S, P (to LDS), dV^T += dO^T P
+  auto p_step = [&](int slot) __attribute__((always_inline)) {
+    const int t = T - 1 - (slot % nT);
     const int r0 = t * BN;
     const unsigned char* qt = qbuf(slot);
     const unsigned char* dt = dbuf(slot);
-    const unsigned char* st = sbuf(slot);
+    const unsigned char* st = sbuf(slot) + h2 * 16;  // this lane's rows 4 h2 .. 4 h2 + 3 of each group
+    unsigned char* pt = pbuf(slot);
     const bool need_mask = (p.causal && r0 < kw0 + 31) || (r0 + BN > N) || (kw0 + 31 >= N);
 #pragma unroll
     for (int rb = 0; rb < C::RB; ++rb) {
-      // S = Q K^T and dP = dO V^T for 32 query rows x this wave's 32 keys:
-      // lane (key c) holds query rows rb*32 + 8 (e/4) + 4 h2 + e%4
-      f32x16_t sc, dp;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sc[e] = dp[e] = 0.f;
-#pragma unroll
-      for (int s = 0; s < C::KS; ++s) {
-        const u32x4_t a = *(const u32x4_t*)(qt + rpart[s] + rb * 32 * C::ROWB);
-        const u32x4_t d = *(const u32x4_t*)(dt + rpart[s] + rb * 32 * C::ROWB);
-        sc = mfma_32x32x16(a, kreg[s], sc);
-        dp = mfma_32x32x16(d, vreg[s], dp);
-      }
-      // P = 2^(S c2 - lse2), dS = P (dP - D); both packed as B operands. The
-      // mask is applied only on the tiles that need it (a uniform choice) and
-      // with bit operations, so no lane-divergent branch enters the loop.
-      u32x4_t pp[2], ds[2];
+      const f32x16_t sc = row_product(qt, rb);
+      u32x4_t pp[2];
       auto make_p = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row4 = rb * 32 + 8 * r + 4 * h2;  // first of this lane's 4 rows in group r
-          const f32x4_t l2 = *(const f32x4_t*)(st + row4 * 4);
-          const f32x4_t dd = *(const f32x4_t*)(st + 256 + row4 * 4);
-          float pv[4], dsv[4];
+          const f32x4_t l2 = *(const f32x4_t*)(st + (rb * 32 + 8 * r) * 4);
+          float pv[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int e = 4 * r + i;
-            float pe = __builtin_amdgcn_exp2f(fmaf(sc[e], c2, -l2[i]));
+            float pe = __builtin_amdgcn_exp2f(fmaf(sc[4 * r + i], c2, -l2[i]));
             if constexpr (decltype(masked)::value) {
               const int qrow = r0 + row4 + i;
               const unsigned vis = (unsigned)(qrow < N) & (unsigned)(kj < N) & (unsigned)(!p.causal | (kj <= qrow));
               pe = __uint_as_float(__float_as_uint(pe) & (0u - vis));
             }
             pv[i] = pe;
-            dsv[i] = pe * (dp[e] - dd[i]);
           }
-          // k-step ps = 2 rb + r/2 holds rows (r even: e 0-7 -> elements 0..3 of
-          // the pack, r odd: 4..7); words 2(r&1), 2(r&1)+1
           const int kk = r >> 1, wd = (r & 1) * 2;
           pp[kk][wd] = pack_bf16x2(pv[0], pv[1]);
           pp[kk][wd + 1] = pack_bf16x2(pv[2], pv[3]);
-          ds[kk][wd] = pack_bf16x2(dsv[0], dsv[1]);
-          ds[kk][wd + 1] = pack_bf16x2(dsv[2], dsv[3]);
         }
       };
       if (need_mask)
         make_p(std::true_type{});
       else
         make_p(std::false_type{});
-      // dV^T += dO^T P and dK^T += Q^T dS (rows d, columns this wave's keys)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int ps = rb * 2 + kk;
+      for (int kk = 0; kk < 2; ++kk) *(u32x4_t*)(pt + (rb * 2 + kk) * 1024 + hand) = pp[kk];
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          dv[db] = mfma_32x32x16(tr_read(dt, ps, db), pp[kk], dv[db]);
-          dk[db] = mfma_32x32x16(tr_read(qt, ps, db), ds[kk], dk[db]);
-        }
-      }
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) grad[db] = mfma_32x32x16(tr_read(dt, rb * 2 + kk, db), pp[kk], grad[db]);
     }
   };
 
-  // ---- the stream: issue slot j+3 at the top of iteration j (into the buffer
-  // of slot j-1); slot j+1 must have landed before the barrier ending j
+  // dS wave, slot j - 1: dS = P (dP - D) with P from LDS, dK^T += Q^T dS
+  auto ds_finish = [&](int slot) __attribute__((always_inline)) {
+    const unsigned char* qt = qbuf(slot);
+    const unsigned char* st = sbuf(slot) + h2 * 16;
+    const unsigned char* pt = pbuf(slot);
+#pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb) {
+      u32x4_t pw[2], ds[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) pw[kk] = *(const u32x4_t*)(pt + (rb * 2 + kk) * 1024 + hand);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const f32x4_t dd = *(const f32x4_t*)(st + 256 + (rb * 32 + 8 * r) * 4);
+        const int kk = r >> 1, wd = (r & 1) * 2;
+        float dsv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const unsigned word = pw[kk][wd + (i >> 1)];
+          const float pe = __uint_as_float((i & 1) ? (word & 0xffff0000u) : (word << 16));
+          dsv[i] = pe * (dp[rb][4 * r + i] - dd[i]);
+        }
+        ds[kk][wd] = pack_bf16x2(dsv[0], dsv[1]);
+        ds[kk][wd + 1] = pack_bf16x2(dsv[2], dsv[3]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) grad[db] = mfma_32x32x16(tr_read(qt, rb * 2 + kk, db), ds[kk], grad[db]);
+    }
+  };
+  // dS wave, slot j: dP = dO V^T, kept for the next slot
+  auto ds_start = [&](int slot) __attribute__((always_inline)) {
+    const unsigned char* dt = dbuf(slot);
+#pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb) dp[rb] = row_product(dt, rb);
+  };
+
+  // ---- the stream: slot j+1 is copied during slot j (into the buffer of
+  // slot j-2, which the dS wave finished in slot j-1); every copy has landed
+  // at the barrier that ends the slot (__syncthreads waits for them). The two
+  // roles run separate copies of the loop (the same barriers in the same
+  // order), so each copy's registers are allocated for its own live values.
   if (n_slots > 0) issue(0);
-  if (n_slots > 1) issue(1);
-  if (n_slots > 2) issue(2);
-  wait_tiles_after(min(n_slots - 1, 2));
+  wait_vmcnt<0>();
   __syncthreads();
-  for (int j = 0; j < n_slots; ++j) {
-    if (j + 3 < n_slots) issue(j + 3);
-    const int r = j % nT;
-    if (wave_live && r <= nT - 1 - w_t0) compute(j);
-    wait_tiles_after(min(n_slots - j - 2, 2));
-    __syncthreads();
+  if (!ds_wave) {
+    for (int j = 0; j <= n_slots; ++j) {
+      if (j + 1 < n_slots) issue(j + 1);
+      if (j < n_slots && live(j)) p_step(j);
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
+  } else {
+    for (int j = 0; j <= n_slots; ++j) {
+      if (j + 1 < n_slots) issue(j + 1);
+      if (j > 0 && live(j - 1)) ds_finish(j - 1);
+      if (j < n_slots && live(j)) ds_start(j);
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
   }
 
-  // ---- epilogue: dK = scale dK^T, dV = dV^T, bf16 rows through LDS ----------------
+  // ---- epilogue: dV = dV^T (P wave), dK = scale dK^T (dS wave), bf16 rows through LDS
   unsigned char* const ost = lds + wave * 32 * C::OROW;
   constexpr int RPI_O = 64 / C::CPR;
-  const float sc_k = p.scale;
+  const float m = ds_wave ? p.scale : 1.f;
 #pragma unroll
-  for (int which = 0; which < 2; ++which) {
+  for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int vq = 0; vq < 4; ++vq) {
-        const f32x16_t& acc = which ? dv[db] : dk[db];
-        const float m = which ? 1.f : sc_k;
-        u32x2_t pk;
-        pk[0] = pack_bf16x2(acc[vq * 4 + 0] * m, acc[vq * 4 + 1] * m);
-        pk[1] = pack_bf16x2(acc[vq * 4 + 2] * m, acc[vq * 4 + 3] * m);
-        *(u32x2_t*)(ost + c * C::OROW + (db * 32 + vq * 8 + h2 * 4) * 2) = pk;
-      }
-    __builtin_amdgcn_wave_barrier();
-    __bf16* og = (__bf16*)(which ? p.dv : p.dk) + b * p.k_sb + kvh * p.k_sh;
-#pragma unroll
-    for (int i = 0; i < 32 / RPI_O; ++i) {
-      const int r = i * RPI_O + lane / C::CPR, ch = lane % C::CPR;
-      const u32x4_t val = *(const u32x4_t*)(ost + r * C::OROW + ch * 16);
-      if (kw0 + r < N) *(u32x4_t*)(og + (long long)(kw0 + r) * p.k_sn + ch * 8) = val;
+    for (int vq = 0; vq < 4; ++vq) {
+      u32x2_t pk;
+      pk[0] = pack_bf16x2(grad[db][vq * 4 + 0] * m, grad[db][vq * 4 + 1] * m);
+      pk[1] = pack_bf16x2(grad[db][vq * 4 + 2] * m, grad[db][vq * 4 + 3] * m);
+      *(u32x2_t*)(ost + c * C::OROW + (db * 32 + vq * 8 + h2 * 4) * 2) = pk;
     }
-    __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_wave_barrier();
+  __bf16* og = (__bf16*)(ds_wave ? p.dk : p.dv) + b * p.k_sb + kvh * p.k_sh;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI_O; ++i) {
+    const int r = i * RPI_O + lane / C::CPR, ch = lane % C::CPR;
+    const u32x4_t val = *(const u32x4_t*)(ost + r * C::OROW + ch * 16);
+    if (kw0 + r < N) *(u32x4_t*)(og + (long long)(kw0 + r) * p.k_sn + ch * 8) = val;
   }
 }
 
@@ -549,7 +605,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p, int n_q
 
 template <int D>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
-  constexpr int NWK = 4, NWQ = 8, BN = 64;
+  constexpr int NPK = 4, NWQ = 8, BN = 64;
   {
     constexpr int CPR = D / 8;
     const long long rows = (long long)p.B * p.Hq * p.Npad;
@@ -560,10 +616,10 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   {
-    const int n_kblk = (p.N + NWK * 32 - 1) / (NWK * 32);
+    const int n_kblk = (p.N + NPK * 32 - 1) / (NPK * 32);
     const long long total = (long long)p.B * p.Hkv * n_kblk;
     if (total <= 0 || total > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NWK, BN>), dim3((unsigned)total), dim3(NWK * 64), 0, stream, p,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NPK, BN>), dim3((unsigned)total), dim3(2 * NPK * 64), 0, stream, p,
                        n_kblk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
