@@ -340,7 +340,7 @@ def backward_report(dev, stream, steps: int) -> dict:
     log(f"backward: {t:.1f} us ({tf:.1f} TFLOP/s)")
     return {"workload": f"{x.name}, dq/dk/dv given dO", "value": round(tf, 3), "unit": "TFLOP/s",
             "avg_call_us": round(t, 2), "flops_per_call": fl,
-            "kernels": "bwd_pre_kernel<128> + bwd_dkdv_kernel<128,4,64> + bwd_dq_kernel<128,8,64>",
+            "kernels": "bwd_dq_kernel<128,8,64> + bwd_dkdv_kernel<128,4,64>",
             "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / BF16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic("backward", BACKWARD_SOURCES)}}
@@ -423,7 +423,7 @@ def write_traffic(root: str) -> int:
                                     DECODE_SOURCES),
                                    ("prefill_paged", "chunked", ["prefill_bf16_kernel"], PREFILL_SOURCES),
                                    ("kv_append", "append", ["kv_append_kernel"], APPEND_SOURCES),
-                                   ("backward", "backward", ["bwd_pre_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"],
+                                   ("backward", "backward", ["bwd_dq_kernel", "bwd_dkdv_kernel"],
                                     BACKWARD_SOURCES),
                                    ("decode_mla", "mla", ["mla_split_kernel", "mla_merge_kernel"], MLA_SOURCES),
                                    ("prefill_d64_hkv16", "c3_16", ["prefill_bf16_kernel"], PREFILL_SOURCES),

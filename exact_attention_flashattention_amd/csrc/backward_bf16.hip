@@ -9,15 +9,15 @@
 // P are recomputed tile by tile instead of stored: P = 2^(S log2(e) - lse2)
 // with the forward's log-sum-exp, so no running max is needed.
 //
-// Three kernels:
-//  * bwd_pre: D_i and lse2_i = lse_i * log2(e) per row, into the workspace.
+// Two kernels, in this order:
+//  * bwd_dq: a work-group owns 32 queries per wave of one (b, h) and streams
+//    the K and V tiles, like the forward. Each wave also forms D_i and
+//    lse2_i = lse_i * log2(e) of its rows and writes them to the workspace.
 //  * bwd_dkdv: a work-group owns 128 keys of one (b, KV head), 32 per pair
 //    of waves, and streams the Q and dO tiles (and their D, lse2) of every
 //    query head of the group through LDS; one wave of a pair keeps dV^T and
 //    the other dK^T in registers, so no atomics.
-//  * bwd_dq: a work-group owns 32 queries per wave of one (b, h) and streams
-//    the K and V tiles, like the forward.
-// Both main kernels copy tiles HBM -> LDS with global_load_lds into a ring
+// Both kernels copy tiles HBM -> LDS with global_load_lds into a ring
 // (one barrier per tile) and read them with the same XOR swizzle
 // as the forward: row reads for the A operand of S = Q K^T / dP = dO V^T and
 // ds_read_b64_tr_b16 transposed reads for the A operand of the dK, dV, dQ
@@ -59,40 +59,6 @@ struct BCfg {
   static_assert(LPT % NW == 0 || NW % LPT == 0, "uneven tile loads");
   static_assert(BN % 32 == 0 && (D == 64 || D == 128), "bad tile");
 };
-
-// ---------------------------------------------------------------------------
-// D_i = sum_d dO_id O_id (fp32) and lse2_i = lse_i * log2(e), rows in
-// [B, Hq, Npad] order (Npad = N rounded up to 64; padding rows get 0).
-template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
-  constexpr int CPR = D / 8;
-  const long long rows = (long long)p.B * p.Hq * p.Npad;
-  const long long row = (long long)blockIdx.x * (256 / CPR) + threadIdx.x / CPR;
-  const int ch = threadIdx.x % CPR;
-  float acc = 0.f, l2 = 0.f;
-  if (row < rows) {
-    const int i = (int)(row % p.Npad);
-    const long long bh = row / p.Npad;
-    const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
-    if (i < p.N) {
-      const long long off = b * p.q_sb + (long long)i * p.q_sn + h * p.q_sh + ch * 8;
-      const u32x4_t ov = *(const u32x4_t*)((const __bf16*)p.o + off);
-      const u32x4_t dv = *(const u32x4_t*)((const __bf16*)p.dout + off);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc += __builtin_bit_cast(float, ov[e] << 16) * __builtin_bit_cast(float, dv[e] << 16);
-        acc += __builtin_bit_cast(float, ov[e] & 0xffff0000u) * __builtin_bit_cast(float, dv[e] & 0xffff0000u);
-      }
-      l2 = p.lse[(bh * p.N) + i] * kLog2e;
-    }
-  }
-#pragma unroll
-  for (int o = CPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-  if (row < rows && ch == 0) {
-    p.dvec[row] = acc;
-    p.lse2[row] = l2;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // dK and dV. Work item = (KV head, b, key block of 32*NP keys); the streamed
@@ -428,20 +394,37 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p, int n_q
   const int qi = qw0 + c;
   const float c2 = p.scale_log2;
 
-  // Q and dO of this lane's row as B operands, and its lse2, D
+  // Q and dO of this lane's row as B operands; D = sum_d dO O of the row
+  // (each lane half holds half of the dimensions) and lse2 = lse log2(e),
+  // also written to the workspace for the dK/dV kernel, which runs after
+  // this one (padding rows up to Npad get 0)
   u32x4_t qreg[C::KS], doreg[C::KS];
-  float l2 = 0.f, dd = 0.f;
+  float l2, dd;
   {
     const int qc = min(qi, N - 1);
     const long long off = b * p.q_sb + (long long)qc * p.q_sn + h * p.q_sh;
+    u32x4_t oreg[C::KS];
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) {
       qreg[s] = *(const u32x4_t*)((const __bf16*)p.q + off + s * 16 + h2 * 8);
       doreg[s] = *(const u32x4_t*)((const __bf16*)p.dout + off + s * 16 + h2 * 8);
+      oreg[s] = __builtin_nontemporal_load((const u32x4_t*)((const __bf16*)p.o + off + s * 16 + h2 * 8));
     }
-    const long long srow = ((long long)b * p.Hq + h) * p.Npad + qc;
-    l2 = p.lse2[srow];
-    dd = p.dvec[srow];
+    const long long bh = (long long)b * p.Hq + h;
+    l2 = p.lse[bh * N + qc] * kLog2e;
+    float part = 0.f;
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        part += __builtin_bit_cast(float, oreg[s][e] << 16) * __builtin_bit_cast(float, doreg[s][e] << 16);
+        part += __builtin_bit_cast(float, oreg[s][e] & 0xffff0000u) * __builtin_bit_cast(float, doreg[s][e] & 0xffff0000u);
+      }
+    dd = halves_sum(part);
+    if (h2 == 0 && qi < p.Npad) {
+      p.dvec[bh * p.Npad + qi] = qi < N ? dd : 0.f;
+      p.lse2[bh * p.Npad + qi] = qi < N ? l2 : 0.f;
+    }
   }
   f32x16_t dq[C::DB];
 #pragma unroll
@@ -606,12 +589,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p, int n_q
 template <int D>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
   constexpr int NPK = 4, NWQ = 8, BN = 64;
-  {
-    constexpr int CPR = D / 8;
-    const long long rows = (long long)p.B * p.Hq * p.Npad;
-    const long long blocks = (rows + 256 / CPR - 1) / (256 / CPR);
-    if (blocks <= 0 || blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  {  // dQ first: it also writes D and lse2 for the dK/dV kernel
+    const int n_qblk = (p.N + NWQ * 32 - 1) / (NWQ * 32);
+    const long long total = (long long)p.B * p.Hq * n_qblk;
+    if (total <= 0 || total > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NWQ, BN>), dim3((unsigned)total), dim3(NWQ * 64), 0, stream, p,
+                       n_qblk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -621,15 +604,6 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
     if (total <= 0 || total > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, NPK, BN>), dim3((unsigned)total), dim3(2 * NPK * 64), 0, stream, p,
                        n_kblk);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  {
-    const int n_qblk = (p.N + NWQ * 32 - 1) / (NWQ * 32);
-    const long long total = (long long)p.B * p.Hq * n_qblk;
-    if (total <= 0 || total > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, NWQ, BN>), dim3((unsigned)total), dim3(NWQ * 64), 0, stream, p,
-                       n_qblk);
   }
   return hipGetLastError();
 }
