@@ -61,9 +61,15 @@ struct BCfg {
 };
 
 // ---------------------------------------------------------------------------
-// dK and dV. Work item = (KV head, b, key block of 32*NP keys); the streamed
-// slots are (query head of the group, query tile) with the tiles that hold a
-// query at or after the block's first key (causal) or all tiles.
+// dK and dV. A key block is 32*NP keys of one (b, KV head); its streamed
+// slots are (query tile, query head of the group) over the tiles that hold a
+// query at or after the block's first key (causal) or all tiles, tile-major.
+// A work item takes key block j with its tiles in descending order and then
+// key block n_kblk-1-j in ascending order. Under the causal mask the two
+// blocks together stream the same number of tiles for every j, and at any
+// time all items of one (b, KV head) stream one of two tiles (tile T-1-r in
+// the first block, tile r-2 in the second, r counted from the item's start),
+// so the work-groups that run side by side share their Q/dO reads in L2.
 //
 // The work of a 32-key block is split over a pair of waves that share a SIMD
 // (waves w and w + NP): the "P wave" w computes S = Q K^T, the weights
@@ -92,9 +98,10 @@ __global__ __launch_bounds__(2 * NP * 64, 1) void bwd_dkdv_kernel(BwdParams p, i
 
   const int g = p.Hq / p.Hkv;
   const int N = p.N;
-  const int w = xcd_remap(blockIdx.x, p.B * p.Hkv * n_kblk);
-  const int pair = w / n_kblk;                 // (kv head, b), b fastest
-  const int kblk = w - pair * n_kblk;
+  const int n_items = (n_kblk + 1) / 2;
+  const int w = xcd_remap(blockIdx.x, p.B * p.Hkv * n_items);
+  const int pair = w / n_items;                // (kv head, b), b fastest
+  const int item = w - pair * n_items;
   const int kvh = pair / p.B, b = pair - kvh * p.B;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -102,266 +109,281 @@ __global__ __launch_bounds__(2 * NP * 64, 1) void bwd_dkdv_kernel(BwdParams p, i
   const int pi = wave % NP;                    // key block of the wave pair
   const bool ds_wave = wave >= NP;
   const int c = lane & 31, h2 = lane >> 5;
-  const int k_blk0 = kblk * NP * 32;
-  const int kw0 = k_blk0 + pi * 32;            // the pair's first key
-  const int kj = kw0 + c;                      // this lane's key (column of S)
-  const float c2 = p.scale_log2;
 
-  // K (P wave) or V (dS wave) of this lane's key as B operands (k-step s:
-  // dims s*16 + h2*8 .. +7)
-  u32x4_t kvreg[C::KS];
-  {
-    const int kc = min(kj, N - 1);
-    const __bf16* src = (const __bf16*)(ds_wave ? p.v : p.k) + b * p.k_sb + (long long)kc * p.k_sn + kvh * p.k_sh;
-#pragma unroll
-    for (int s = 0; s < C::KS; ++s) kvreg[s] = *(const u32x4_t*)(src + s * 16 + h2 * 8);
-  }
-  f32x16_t grad[C::DB];  // dV^T (P wave) or dK^T / scale (dS wave)
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) grad[db][e] = 0.f;
-  f32x16_t dp[C::RB];  // dS wave: dP of the current slot, carried into the next
-#pragma unroll
-  for (int rb = 0; rb < C::RB; ++rb)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) dp[rb][e] = 0.f;
+  // one key block, its tiles descending or ascending
+  auto run_block = [&](const int kblk, const bool desc) __attribute__((always_inline)) {
+    const int k_blk0 = kblk * NP * 32;
+    const int kw0 = k_blk0 + pi * 32;            // the pair's first key
+    const int kj = kw0 + c;                      // this lane's key (column of S)
+    const float c2 = p.scale_log2;
 
-  // streamed slots: (query head hg, query tile T - 1 - r). The tiles of a
-  // head run from the last one down to the block's first, so the work-groups
-  // of one (b, KV head), which run side by side, start on the same last tile
-  // and L2 serves most of their Q/dO reads.
-  const int T = (N + BN - 1) / BN;
-  const int t0 = p.causal ? k_blk0 / BN : 0;
-  const int nT = T - t0;
-  const int n_slots = g * nT;
-  const int w_t0 = (p.causal ? kw0 / BN : 0) - t0;  // the pair's first tile within a head's run
-  const bool pair_live = kw0 < N;
-  auto live = [&](int slot) __attribute__((always_inline)) {
-    return pair_live && (slot % nT) <= nT - 1 - w_t0;
-  };
+    // K (P wave) or V (dS wave) of this lane's key as B operands (k-step s:
+    // dims s*16 + h2*8 .. +7)
+    u32x4_t kvreg[C::KS];
+    {
+      const int kc = min(kj, N - 1);
+      const __bf16* src = (const __bf16*)(ds_wave ? p.v : p.k) + b * p.k_sb + (long long)kc * p.k_sn + kvh * p.k_sh;
+  #pragma unroll
+      for (int s = 0; s < C::KS; ++s) kvreg[s] = *(const u32x4_t*)(src + s * 16 + h2 * 8);
+    }
+    f32x16_t grad[C::DB];  // dV^T (P wave) or dK^T / scale (dS wave)
+  #pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+  #pragma unroll
+      for (int e = 0; e < 16; ++e) grad[db][e] = 0.f;
+    f32x16_t dp[C::RB];  // dS wave: dP of the current slot, carried into the next
+  #pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb)
+  #pragma unroll
+      for (int e = 0; e < 16; ++e) dp[rb][e] = 0.f;
 
-  // Buffer addresses of a slot. The offset goes through an empty asm
-  // statement so that it is formed once per slot in a scalar register: left
-  // to itself the compiler precomputes every (buffer, lane offset) sum as a
-  // loop-invariant vector register (most exceed the 16-bit immediate offset
-  // of the LDS instructions) and runs out of registers.
-  auto at = [&](unsigned off) __attribute__((always_inline)) {
-    asm volatile("" : "+s"(off));
-    return lds + off;
-  };
-  auto qbuf = [&](int s) __attribute__((always_inline)) { return at((unsigned)(s % NB) * C::TILE); };
-  auto dbuf = [&](int s) __attribute__((always_inline)) { return at(RING + (unsigned)(s % NB) * C::TILE); };
-  auto sbuf = [&](int s) __attribute__((always_inline)) { return at(SREG + (unsigned)(s % NB) * SBUF + wave * 1024); };
-  auto pbuf = [&](int s) __attribute__((always_inline)) { return at(PREG + (unsigned)(s & 1) * PSLOT + pi * PPAIR); };
+    // streamed slots: slot s is query head s % g of tile rank r = s / g, the
+    // tile T - 1 - r (descending) or t0 + r (ascending)
+    const int T = (N + BN - 1) / BN;
+    const int t0 = p.causal ? k_blk0 / BN : 0;
+    const int nT = T - t0;
+    const int n_slots = g * nT;
+    const int w_t = p.causal ? kw0 / BN : 0;  // the pair's first tile
+    const bool pair_live = kw0 < N;
+    auto tile_of = [&](int slot) __attribute__((always_inline)) {
+      const int r = slot / g;
+      return desc ? T - 1 - r : t0 + r;
+    };
+    auto live = [&](int slot) __attribute__((always_inline)) { return pair_live && tile_of(slot) >= w_t; };
 
-  const int ld_row = lane / C::CPR, ld_pos = lane % C::CPR;
-  const unsigned row_bytes = (unsigned)p.q_sn * 2u;
-  unsigned ld_off[C::IPW];
-#pragma unroll
-  for (int u = 0; u < C::IPW; ++u) {
-    const int row = (wave + u * NW) * C::RPI + ld_row;
-    ld_off[u] = (unsigned)row * row_bytes + (unsigned)(ld_pos ^ swz<C::CPR>(row)) * 16u;
-  }
-  auto issue = [&](int slot) __attribute__((always_inline)) {
-    const int hg = slot / nT, t = T - 1 - (slot - hg * nT);
-    const int h = kvh * g + hg;
-    const int r0 = t * BN;
-    const char* qt = (const char*)((const __bf16*)p.q + b * p.q_sb + h * p.q_sh) + (long long)r0 * row_bytes;
-    const char* dt = (const char*)((const __bf16*)p.dout + b * p.q_sb + h * p.q_sh) + (long long)r0 * row_bytes;
-    const bool ragged = r0 + BN > N;
-#pragma unroll
+    // Buffer addresses of a slot. The offset goes through an empty asm
+    // statement so that it is formed once per slot in a scalar register: left
+    // to itself the compiler precomputes every (buffer, lane offset) sum as a
+    // loop-invariant vector register (most exceed the 16-bit immediate offset
+    // of the LDS instructions) and runs out of registers.
+    auto at = [&](unsigned off) __attribute__((always_inline)) {
+      asm volatile("" : "+s"(off));
+      return lds + off;
+    };
+    auto qbuf = [&](int s) __attribute__((always_inline)) { return at((unsigned)(s % NB) * C::TILE); };
+    auto dbuf = [&](int s) __attribute__((always_inline)) { return at(RING + (unsigned)(s % NB) * C::TILE); };
+    auto sbuf = [&](int s) __attribute__((always_inline)) {
+      return at(SREG + (unsigned)(s % NB) * SBUF + wave * 1024);
+    };
+    auto pbuf = [&](int s) __attribute__((always_inline)) {
+      return at(PREG + (unsigned)(s & 1) * PSLOT + pi * PPAIR);
+    };
+
+    const int ld_row = lane / C::CPR, ld_pos = lane % C::CPR;
+    const unsigned row_bytes = (unsigned)p.q_sn * 2u;
+    unsigned ld_off[C::IPW];
+  #pragma unroll
     for (int u = 0; u < C::IPW; ++u) {
-      const int i = wave + u * NW;
-      if (C::LPT < NW && i >= C::LPT) break;
-      unsigned off = ld_off[u];
-      if (ragged) {  // rows past the end repeat the last row (finite); they are masked
-        const int row = i * C::RPI + ld_row;
-        off = (unsigned)(min(r0 + row, N - 1) - r0) * row_bytes + (unsigned)(ld_pos ^ swz<C::CPR>(row)) * 16u;
-      }
-      load_to_lds(qt + off, qbuf(slot) + i * 1024);
-      load_to_lds(dt + off, dbuf(slot) + i * 1024);
+      const int row = (wave + u * NW) * C::RPI + ld_row;
+      ld_off[u] = (unsigned)row * row_bytes + (unsigned)(ld_pos ^ swz<C::CPR>(row)) * 16u;
     }
-    // stats rows r0 .. r0+63 (padded arrays): lanes 0-15 lse2, 16-31 D, 32-63 again
-    const long long srow = ((long long)b * p.Hq + h) * p.Npad + r0;
-    const int l32 = lane & 31;
-    const float* src = (l32 < 16 ? p.lse2 : p.dvec) + srow + (l32 & 15) * 4;
-    load_to_lds(src, sbuf(slot));
-  };
-
-  // per-lane parts of the LDS reads (bytes from a tile's start)
-  unsigned rpart[C::KS];  // row reads: row c (+32 per block), chunk (2s + h2) ^ swz(c)
-#pragma unroll
-  for (int s = 0; s < C::KS; ++s) rpart[s] = (unsigned)(c * C::ROWB + (((2 * s + h2) ^ swz<C::CPR>(c)) * 16));
-  unsigned tpart[2][C::DB];  // transposed reads: rows ps*16 + 8r + 4h2 + t, dims db*32 + 16G + 4u
-  {
-    const int tr_t = (lane >> 2) & 3, tr_u = lane & 3, tr_g = (lane >> 4) & 1;
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const int row = 8 * r + 4 * h2 + tr_t;
-        const int d = db * 32 + 16 * tr_g + 4 * tr_u;
-        tpart[r][db] = (unsigned)(row * C::ROWB + ((d >> 3) ^ swz<C::CPR>(row)) * 16 + ((d >> 2) & 1) * 8);
+    auto issue = [&](int slot) __attribute__((always_inline)) {
+      const int hg = slot % g, t = tile_of(slot);
+      const int h = kvh * g + hg;
+      const int r0 = t * BN;
+      const char* qt = (const char*)((const __bf16*)p.q + b * p.q_sb + h * p.q_sh) + (long long)r0 * row_bytes;
+      const char* dt = (const char*)((const __bf16*)p.dout + b * p.q_sb + h * p.q_sh) + (long long)r0 * row_bytes;
+      const bool ragged = r0 + BN > N;
+  #pragma unroll
+      for (int u = 0; u < C::IPW; ++u) {
+        const int i = wave + u * NW;
+        if (C::LPT < NW && i >= C::LPT) break;
+        unsigned off = ld_off[u];
+        if (ragged) {  // rows past the end repeat the last row (finite); they are masked
+          const int row = i * C::RPI + ld_row;
+          off = (unsigned)(min(r0 + row, N - 1) - r0) * row_bytes + (unsigned)(ld_pos ^ swz<C::CPR>(row)) * 16u;
+        }
+        load_to_lds(qt + off, qbuf(slot) + i * 1024);
+        load_to_lds(dt + off, dbuf(slot) + i * 1024);
       }
-  }
-  auto tr_read = [&](const unsigned char* base, int ps, int db) __attribute__((always_inline)) {
-    u32x4_t a;
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const s16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4_t*)(base + tpart[r][db] + ps * 16 * C::ROWB));
-      const u32x2_t xx = __builtin_bit_cast(u32x2_t, x);
-      a[2 * r] = xx[0];
-      a[2 * r + 1] = xx[1];
-    }
-    return a;
-  };
-  // 32 rows of a streamed tile times this pair's 32 keys: lane (key c) holds
-  // query rows rb*32 + 8 (e/4) + 4 h2 + e%4
-  auto row_product = [&](const unsigned char* tile, int rb) __attribute__((always_inline)) {
-    f32x16_t acc;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-#pragma unroll
-    for (int s = 0; s < C::KS; ++s)
-      acc = mfma_32x32x16(*(const u32x4_t*)(tile + rpart[s] + rb * 32 * C::ROWB), kvreg[s], acc);
-    return acc;
-  };
-  // P and dS words, in the accumulator's lane layout: k-step ps = 2 rb + kk
-  // holds the rows of groups r = 2 kk, 2 kk + 1 (words 2(r&1), 2(r&1)+1), so
-  // the packed words are the B operand of the transposed products as they are
-  const int hand = lane * 16;  // byte offset of this lane's 16 bytes in a 1 KiB hand-over block
+      // stats rows r0 .. r0+63 (padded arrays): lanes 0-15 lse2, 16-31 D, 32-63 again
+      const long long srow = ((long long)b * p.Hq + h) * p.Npad + r0;
+      const int l32 = lane & 31;
+      const float* src = (l32 < 16 ? p.lse2 : p.dvec) + srow + (l32 & 15) * 4;
+      load_to_lds(src, sbuf(slot));
+    };
 
-  // P wave, slot j: S, P (to LDS), dV^T += dO^T P
-  auto p_step = [&](int slot) __attribute__((always_inline)) {
-    const int t = T - 1 - (slot % nT);
-    const int r0 = t * BN;
-    const unsigned char* qt = qbuf(slot);
-    const unsigned char* dt = dbuf(slot);
-    const unsigned char* st = sbuf(slot) + h2 * 16;  // this lane's rows 4 h2 .. 4 h2 + 3 of each group
-    unsigned char* pt = pbuf(slot);
-    const bool need_mask = (p.causal && r0 < kw0 + 31) || (r0 + BN > N) || (kw0 + 31 >= N);
-#pragma unroll
-    for (int rb = 0; rb < C::RB; ++rb) {
-      const f32x16_t sc = row_product(qt, rb);
-      u32x4_t pp[2];
-      auto make_p = [&](auto masked) __attribute__((always_inline)) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row4 = rb * 32 + 8 * r + 4 * h2;  // first of this lane's 4 rows in group r
-          const f32x4_t l2 = *(const f32x4_t*)(st + (rb * 32 + 8 * r) * 4);
-          float pv[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float pe = __builtin_amdgcn_exp2f(fmaf(sc[4 * r + i], c2, -l2[i]));
-            if constexpr (decltype(masked)::value) {
-              const int qrow = r0 + row4 + i;
-              const unsigned vis = (unsigned)(qrow < N) & (unsigned)(kj < N) & (unsigned)(!p.causal | (kj <= qrow));
-              pe = __uint_as_float(__float_as_uint(pe) & (0u - vis));
+    // per-lane parts of the LDS reads (bytes from a tile's start)
+    unsigned rpart[C::KS];  // row reads: row c (+32 per block), chunk (2s + h2) ^ swz(c)
+  #pragma unroll
+    for (int s = 0; s < C::KS; ++s) rpart[s] = (unsigned)(c * C::ROWB + (((2 * s + h2) ^ swz<C::CPR>(c)) * 16));
+    unsigned tpart[2][C::DB];  // transposed reads: rows ps*16 + 8r + 4h2 + t, dims db*32 + 16G + 4u
+    {
+      const int tr_t = (lane >> 2) & 3, tr_u = lane & 3, tr_g = (lane >> 4) & 1;
+  #pragma unroll
+      for (int r = 0; r < 2; ++r)
+  #pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const int row = 8 * r + 4 * h2 + tr_t;
+          const int d = db * 32 + 16 * tr_g + 4 * tr_u;
+          tpart[r][db] = (unsigned)(row * C::ROWB + ((d >> 3) ^ swz<C::CPR>(row)) * 16 + ((d >> 2) & 1) * 8);
+        }
+    }
+    auto tr_read = [&](const unsigned char* base, int ps, int db) __attribute__((always_inline)) {
+      u32x4_t a;
+  #pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const s16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(base + tpart[r][db] + ps * 16 * C::ROWB));
+        const u32x2_t xx = __builtin_bit_cast(u32x2_t, x);
+        a[2 * r] = xx[0];
+        a[2 * r + 1] = xx[1];
+      }
+      return a;
+    };
+    // 32 rows of a streamed tile times this pair's 32 keys: lane (key c) holds
+    // query rows rb*32 + 8 (e/4) + 4 h2 + e%4
+    auto row_product = [&](const unsigned char* tile, int rb) __attribute__((always_inline)) {
+      f32x16_t acc;
+  #pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  #pragma unroll
+      for (int s = 0; s < C::KS; ++s)
+        acc = mfma_32x32x16(*(const u32x4_t*)(tile + rpart[s] + rb * 32 * C::ROWB), kvreg[s], acc);
+      return acc;
+    };
+    // P and dS words, in the accumulator's lane layout: k-step ps = 2 rb + kk
+    // holds the rows of groups r = 2 kk, 2 kk + 1 (words 2(r&1), 2(r&1)+1), so
+    // the packed words are the B operand of the transposed products as they are
+    const int hand = lane * 16;  // byte offset of this lane's 16 bytes in a 1 KiB hand-over block
+
+    // P wave, slot j: S, P (to LDS), dV^T += dO^T P
+    auto p_step = [&](int slot) __attribute__((always_inline)) {
+      const int t = tile_of(slot);
+      const int r0 = t * BN;
+      const unsigned char* qt = qbuf(slot);
+      const unsigned char* dt = dbuf(slot);
+      const unsigned char* st = sbuf(slot) + h2 * 16;  // this lane's rows 4 h2 .. 4 h2 + 3 of each group
+      unsigned char* pt = pbuf(slot);
+      const bool need_mask = (p.causal && r0 < kw0 + 31) || (r0 + BN > N) || (kw0 + 31 >= N);
+  #pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb) {
+        const f32x16_t sc = row_product(qt, rb);
+        u32x4_t pp[2];
+        auto make_p = [&](auto masked) __attribute__((always_inline)) {
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row4 = rb * 32 + 8 * r + 4 * h2;  // first of this lane's 4 rows in group r
+            const f32x4_t l2 = *(const f32x4_t*)(st + (rb * 32 + 8 * r) * 4);
+            float pv[4];
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float pe = __builtin_amdgcn_exp2f(fmaf(sc[4 * r + i], c2, -l2[i]));
+              if constexpr (decltype(masked)::value) {
+                const int qrow = r0 + row4 + i;
+                const unsigned vis = (unsigned)(qrow < N) & (unsigned)(kj < N) & (unsigned)(!p.causal | (kj <= qrow));
+                pe = __uint_as_float(__float_as_uint(pe) & (0u - vis));
+              }
+              pv[i] = pe;
             }
-            pv[i] = pe;
+            const int kk = r >> 1, wd = (r & 1) * 2;
+            pp[kk][wd] = pack_bf16x2(pv[0], pv[1]);
+            pp[kk][wd + 1] = pack_bf16x2(pv[2], pv[3]);
           }
-          const int kk = r >> 1, wd = (r & 1) * 2;
-          pp[kk][wd] = pack_bf16x2(pv[0], pv[1]);
-          pp[kk][wd + 1] = pack_bf16x2(pv[2], pv[3]);
-        }
-      };
-      if (need_mask)
-        make_p(std::true_type{});
-      else
-        make_p(std::false_type{});
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) *(u32x4_t*)(pt + (rb * 2 + kk) * 1024 + hand) = pp[kk];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) grad[db] = mfma_32x32x16(tr_read(dt, rb * 2 + kk, db), pp[kk], grad[db]);
-    }
-  };
-
-  // dS wave, slot j - 1: dS = P (dP - D) with P from LDS, dK^T += Q^T dS
-  auto ds_finish = [&](int slot) __attribute__((always_inline)) {
-    const unsigned char* qt = qbuf(slot);
-    const unsigned char* st = sbuf(slot) + h2 * 16;
-    const unsigned char* pt = pbuf(slot);
-#pragma unroll
-    for (int rb = 0; rb < C::RB; ++rb) {
-      u32x4_t pw[2], ds[2];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) pw[kk] = *(const u32x4_t*)(pt + (rb * 2 + kk) * 1024 + hand);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const f32x4_t dd = *(const f32x4_t*)(st + 256 + (rb * 32 + 8 * r) * 4);
-        const int kk = r >> 1, wd = (r & 1) * 2;
-        float dsv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const unsigned word = pw[kk][wd + (i >> 1)];
-          const float pe = __uint_as_float((i & 1) ? (word & 0xffff0000u) : (word << 16));
-          dsv[i] = pe * (dp[rb][4 * r + i] - dd[i]);
-        }
-        ds[kk][wd] = pack_bf16x2(dsv[0], dsv[1]);
-        ds[kk][wd + 1] = pack_bf16x2(dsv[2], dsv[3]);
+        };
+        if (need_mask)
+          make_p(std::true_type{});
+        else
+          make_p(std::false_type{});
+  #pragma unroll
+        for (int kk = 0; kk < 2; ++kk) *(u32x4_t*)(pt + (rb * 2 + kk) * 1024 + hand) = pp[kk];
+  #pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+  #pragma unroll
+          for (int db = 0; db < C::DB; ++db) grad[db] = mfma_32x32x16(tr_read(dt, rb * 2 + kk, db), pp[kk], grad[db]);
       }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) grad[db] = mfma_32x32x16(tr_read(qt, rb * 2 + kk, db), ds[kk], grad[db]);
-    }
-  };
-  // dS wave, slot j: dP = dO V^T, kept for the next slot
-  auto ds_start = [&](int slot) __attribute__((always_inline)) {
-    const unsigned char* dt = dbuf(slot);
-#pragma unroll
-    for (int rb = 0; rb < C::RB; ++rb) dp[rb] = row_product(dt, rb);
-  };
+    };
 
-  // ---- the stream: slot j+1 is copied during slot j (into the buffer of
-  // slot j-2, which the dS wave finished in slot j-1); every copy has landed
-  // at the barrier that ends the slot (__syncthreads waits for them). The two
-  // roles run separate copies of the loop (the same barriers in the same
-  // order), so each copy's registers are allocated for its own live values.
-  if (n_slots > 0) issue(0);
-  wait_vmcnt<0>();
-  __syncthreads();
-  if (!ds_wave) {
-    for (int j = 0; j <= n_slots; ++j) {
-      if (j + 1 < n_slots) issue(j + 1);
-      if (j < n_slots && live(j)) p_step(j);
-      wait_vmcnt<0>();
-      __syncthreads();
-    }
-  } else {
-    for (int j = 0; j <= n_slots; ++j) {
-      if (j + 1 < n_slots) issue(j + 1);
-      if (j > 0 && live(j - 1)) ds_finish(j - 1);
-      if (j < n_slots && live(j)) ds_start(j);
-      wait_vmcnt<0>();
-      __syncthreads();
-    }
-  }
+    // dS wave, slot j - 1: dS = P (dP - D) with P from LDS, dK^T += Q^T dS
+    auto ds_finish = [&](int slot) __attribute__((always_inline)) {
+      const unsigned char* qt = qbuf(slot);
+      const unsigned char* st = sbuf(slot) + h2 * 16;
+      const unsigned char* pt = pbuf(slot);
+  #pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb) {
+        u32x4_t pw[2], ds[2];
+  #pragma unroll
+        for (int kk = 0; kk < 2; ++kk) pw[kk] = *(const u32x4_t*)(pt + (rb * 2 + kk) * 1024 + hand);
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const f32x4_t dd = *(const f32x4_t*)(st + 256 + (rb * 32 + 8 * r) * 4);
+          const int kk = r >> 1, wd = (r & 1) * 2;
+          float dsv[4];
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const unsigned word = pw[kk][wd + (i >> 1)];
+            const float pe = __uint_as_float((i & 1) ? (word & 0xffff0000u) : (word << 16));
+            dsv[i] = pe * (dp[rb][4 * r + i] - dd[i]);
+          }
+          ds[kk][wd] = pack_bf16x2(dsv[0], dsv[1]);
+          ds[kk][wd + 1] = pack_bf16x2(dsv[2], dsv[3]);
+        }
+  #pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+  #pragma unroll
+          for (int db = 0; db < C::DB; ++db) grad[db] = mfma_32x32x16(tr_read(qt, rb * 2 + kk, db), ds[kk], grad[db]);
+      }
+    };
+    // dS wave, slot j: dP = dO V^T, kept for the next slot
+    auto ds_start = [&](int slot) __attribute__((always_inline)) {
+      const unsigned char* dt = dbuf(slot);
+  #pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb) dp[rb] = row_product(dt, rb);
+    };
 
-  // ---- epilogue: dV = dV^T (P wave), dK = scale dK^T (dS wave), bf16 rows through LDS
-  unsigned char* const ost = lds + wave * 32 * C::OROW;
-  constexpr int RPI_O = 64 / C::CPR;
-  const float m = ds_wave ? p.scale : 1.f;
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-    for (int vq = 0; vq < 4; ++vq) {
-      u32x2_t pk;
-      pk[0] = pack_bf16x2(grad[db][vq * 4 + 0] * m, grad[db][vq * 4 + 1] * m);
-      pk[1] = pack_bf16x2(grad[db][vq * 4 + 2] * m, grad[db][vq * 4 + 3] * m);
-      *(u32x2_t*)(ost + c * C::OROW + (db * 32 + vq * 8 + h2 * 4) * 2) = pk;
+    // ---- the stream: slot j+1 is copied during slot j (into the buffer of
+    // slot j-2, which the dS wave finished in slot j-1); every copy has landed
+    // at the barrier that ends the slot (__syncthreads waits for them). The two
+    // roles run separate copies of the loop (the same barriers in the same
+    // order), so each copy's registers are allocated for its own live values.
+    if (n_slots > 0) issue(0);
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (!ds_wave) {
+      for (int j = 0; j <= n_slots; ++j) {
+        if (j + 1 < n_slots) issue(j + 1);
+        if (j < n_slots && live(j)) p_step(j);
+        wait_vmcnt<0>();
+        __syncthreads();
+      }
+    } else {
+      for (int j = 0; j <= n_slots; ++j) {
+        if (j + 1 < n_slots) issue(j + 1);
+        if (j > 0 && live(j - 1)) ds_finish(j - 1);
+        if (j < n_slots && live(j)) ds_start(j);
+        wait_vmcnt<0>();
+        __syncthreads();
+      }
     }
-  __builtin_amdgcn_wave_barrier();
-  __bf16* og = (__bf16*)(ds_wave ? p.dk : p.dv) + b * p.k_sb + kvh * p.k_sh;
-#pragma unroll
-  for (int i = 0; i < 32 / RPI_O; ++i) {
-    const int r = i * RPI_O + lane / C::CPR, ch = lane % C::CPR;
-    const u32x4_t val = *(const u32x4_t*)(ost + r * C::OROW + ch * 16);
-    if (kw0 + r < N) *(u32x4_t*)(og + (long long)(kw0 + r) * p.k_sn + ch * 8) = val;
+
+    // ---- epilogue: dV = dV^T (P wave), dK = scale dK^T (dS wave), bf16 rows through LDS
+    unsigned char* const ost = lds + wave * 32 * C::OROW;
+    constexpr int RPI_O = 64 / C::CPR;
+    const float m = ds_wave ? p.scale : 1.f;
+  #pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+  #pragma unroll
+      for (int vq = 0; vq < 4; ++vq) {
+        u32x2_t pk;
+        pk[0] = pack_bf16x2(grad[db][vq * 4 + 0] * m, grad[db][vq * 4 + 1] * m);
+        pk[1] = pack_bf16x2(grad[db][vq * 4 + 2] * m, grad[db][vq * 4 + 3] * m);
+        *(u32x2_t*)(ost + c * C::OROW + (db * 32 + vq * 8 + h2 * 4) * 2) = pk;
+      }
+    __builtin_amdgcn_wave_barrier();
+    __bf16* og = (__bf16*)(ds_wave ? p.dk : p.dv) + b * p.k_sb + kvh * p.k_sh;
+  #pragma unroll
+    for (int i = 0; i < 32 / RPI_O; ++i) {
+      const int r = i * RPI_O + lane / C::CPR, ch = lane % C::CPR;
+      const u32x4_t val = *(const u32x4_t*)(ost + r * C::OROW + ch * 16);
+      if (kw0 + r < N) *(u32x4_t*)(og + (long long)(kw0 + r) * p.k_sn + ch * 8) = val;
+    }
+  };  // run_block
+
+  run_block(item, true);
+  const int second = n_kblk - 1 - item;
+  if (second != item) {
+    __syncthreads();  // the epilogue's staging area overlaps the ring
+    run_block(second, false);
   }
 }
 
@@ -600,7 +622,7 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
   }
   {
     const int n_kblk = (p.N + NPK * 32 - 1) / (NPK * 32);
-    const long long total = (long long)p.B * p.Hkv * n_kblk;
+    const long long total = (long long)p.B * p.Hkv * ((n_kblk + 1) / 2);
     if (total <= 0 || total > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, NPK, BN>), dim3((unsigned)total), dim3(2 * NPK * 64), 0, stream, p,
                        n_kblk);
