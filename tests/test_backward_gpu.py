@@ -66,6 +66,8 @@ CASES = [
     (1, 513, 8, 1, 128, True, "BNHD"),    # MQA, several key blocks and query tiles
     (1, 129, 6, 3, 64, True, "BHND"),
     (1, 256, 4, 2, 128, False, "BHND"),   # tile-aligned, full attention
+    (1, 640, 16, 1, 128, True, "BNHD"),   # g = 16, an odd number of 128-key blocks (one runs alone)
+    (2, 384, 8, 2, 64, False, "BHND"),    # three key blocks, full attention
 ]
 
 
