@@ -258,11 +258,14 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaParams p) {
 }  // namespace
 
 int mla_auto_splits(int B, int Hq, int max_pages_per_seq) {
-  // about 2 work-groups per CU, with at least 64 pages (1024 tokens) per split
-  // so that a split's partial (Hq x 514 floats) stays small next to its K/V
+  // one round of work-groups, at most 256 (the CU count; one work-group fits
+  // a CU), with at least 48 pages (768 tokens) of the table's width per split
+  // so that a split's partial (Hq x 514 floats) stays small next to its rows.
+  // Measured on the 16-sequence workload: 16 splits (256 work-groups)
+  // 105-112 us, 15 splits 107-120 us, 20 to 32 splits 125-135 us.
   const long long chunks = (long long)B * ((Hq + NWM * HPW - 1) / (NWM * HPW));
-  long long s = (512 + chunks - 1) / chunks;
-  const long long cap = max(1, max_pages_per_seq / 64);
+  long long s = 256 / chunks;
+  const long long cap = max(1, max_pages_per_seq / 48);
   if (s > cap) s = cap;
   if (s < 1) s = 1;
   return (int)s;

@@ -286,7 +286,8 @@ def test_decode_mla_sizes(L):
     assert L.attn_decode_mla_num_splits(4, 128, 100, 7) == 7
     assert L.attn_decode_mla_num_splits(4, 128, 5, 7) == 5
     auto = L.attn_decode_mla_num_splits(16, 128, 1024, 0)
-    assert 1 <= auto <= 1024 // 64
+    assert auto == 16  # one round of 256 work-groups (16 sequences x 16 splits)
+    assert L.attn_decode_mla_num_splits(1, 128, 1024, 0) == 1024 // 48  # at least 48 pages per split
     assert L.attn_decode_mla_workspace_size(16, 128, 1024, 0) == 16 * 128 * auto * 514 * 4
     assert L.attn_decode_mla_workspace_size(16, 120, 1024, 0) == 0
 
