@@ -459,8 +459,17 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p, int n_q
   const int n_tiles = p.causal ? min(k_tiles, q_last / BN + 1) : k_tiles;
   const int wave_tiles = (qw0 >= N) ? 0 : (p.causal ? min(n_tiles, (qw0 + 31) / BN + 1) : n_tiles);
 
-  auto kbuf = [&](int t) __attribute__((always_inline)) { return lds + (t % C::NBUF) * C::TILE; };
-  auto vbuf = [&](int t) __attribute__((always_inline)) { return lds + C::BREG + (t % C::NBUF) * C::TILE; };
+  // ring slot t holds K at kbuf(t) and V right after it, at kbuf(t) + TILE, so
+  // the K and V reads of one lane share an address register and differ by an
+  // immediate offset; the slot's base goes through an empty asm statement so
+  // that it is formed once per tile in a scalar register (left to itself the
+  // compiler forms every (slot, lane offset) sum in a vector register)
+  auto kbuf = [&](int t) __attribute__((always_inline)) {
+    unsigned off = (unsigned)(t % C::NBUF) * (2 * C::TILE);
+    asm volatile("" : "+s"(off));
+    return lds + off;
+  };
+  auto vbuf = [&](int t) __attribute__((always_inline)) { return kbuf(t) + C::TILE; };
   const int ld_row = lane / C::CPR, ld_pos = lane % C::CPR;
   const unsigned row_bytes = (unsigned)p.k_sn * 2u;
   unsigned ld_off[C::IPW];
@@ -528,7 +537,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdParams p, int n_q
   auto compute = [&](int t) __attribute__((always_inline)) {
     const int k0 = t * BN;
     const unsigned char* kt = kbuf(t);
-    const unsigned char* vt = vbuf(t);
+    const unsigned char* vt = kt + C::TILE;  // (one base for both)
     const bool need_mask = (p.causal && k0 + BN - 1 > qw0) || (k0 + BN > N);
 #pragma unroll
     for (int kb = 0; kb < C::RB; ++kb) {
