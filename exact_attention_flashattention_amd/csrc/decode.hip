@@ -24,13 +24,19 @@
 //    order, so each page (all KV heads of 16 tokens) is read by one CU at
 //    about the same time, as whole contiguous rows. The K/V of a page slice
 //    are read from HBM once and shared by all query heads of the unit.
+//  * K and V are loaded in 16-byte chunks laid out along the slot rows, so
+//    every load instruction covers whole 2*D-byte rows (whole cache lines),
+//    and staged through per-wave LDS regions. (Loading K straight into the
+//    MFMA operand layout makes each instruction touch half of 16 different
+//    lines; a streaming probe of the two patterns ran 5.8 against 7.0 TB/s,
+//    and the long-context decode 311 -> 300 us with the staged K.)
 //  * Scores for a page are S^T (16 slots x 16 heads) = K q^T with
-//    v_mfma_f32_16x16x32_bf16; the K operand is loaded straight from HBM in
-//    the MFMA layout (16-byte loads). Unused head columns carry q = 0.
-//  * V is staged through a per-wave LDS region and read back transposed for
-//    O^T (d x heads) += V^T P^T with v_mfma_f32_16x16x16_bf16; slots past the
-//    end of the sequence are written as zeros so that a NaN left in an unused
-//    slot cannot reach the output (0 * NaN would).
+//    v_mfma_f32_16x16x32_bf16, the K operand read back from LDS. Unused head
+//    columns carry q = 0.
+//  * V is read back transposed for O^T (d x heads) += V^T P^T with
+//    v_mfma_f32_16x16x16_bf16; slots past the end of the sequence are
+//    staged as zeros so that a NaN left in an unused slot cannot reach the
+//    output (0 * NaN would).
 //  * K and V are read with non-temporal loads: every cached byte is read once
 //    per call, so it should not displace what other kernels keep in the
 //    caches (measured: 330 -> 313 us for the long-context decode).
@@ -100,7 +106,7 @@ struct DCfg {
 template <int D>
 __global__ __launch_bounds__(NWU * 64, ATTN_DECODE_WAVES_PER_SIMD) void decode_split_kernel(DecodeParams p, int HG) {
   using C = DCfg<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[NWU * C::VPAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * NWU * C::VPAGE];
 
   const int S = p.num_splits;
   const int units = p.Hkv * HG;
@@ -162,6 +168,7 @@ __global__ __launch_bounds__(NWU * 64, ATTN_DECODE_WAVES_PER_SIMD) void decode_s
   float m_run = kNegInf, l_run = 0.f;
 
   unsigned char* const vst = lds + wave * C::VPAGE;
+  unsigned char* const kst = lds + (NWU + wave) * C::VPAGE;
 
   // Block-table entries of this wave's pages, 64 at a time in one VGPR (lane t
   // holds the entry of page tbase + t), so a page's loads never wait on a
@@ -175,37 +182,41 @@ __global__ __launch_bounds__(NWU * 64, ATTN_DECODE_WAVES_PER_SIMD) void decode_s
     }
     return __builtin_amdgcn_readlane(tcache, pg - tbase);
   };
-  auto load_page = [&](int pg, u32x4_t (&kr)[C::KS], u32x4_t (&vr)[C::VCH]) {
+  auto load_page = [&](int pg, u32x4_t (&kr)[C::VCH], u32x4_t (&vr)[C::VCH]) {
     const int phys = phys_of(pg);
-#pragma unroll
-    for (int s = 0; s < C::KS; ++s)
-      kr[s] = __builtin_nontemporal_load((const u32x4_t*)(kp + kv_row_offset(phys, j, kvh, p.Hkv, D) + s * 32 + rg * 8));
+    // K and V both as whole 16-byte chunks of consecutive slot rows (each
+    // load instruction covers 64 / (D / 8) slots x 2 D bytes, whole cache lines)
 #pragma unroll
     for (int i = 0; i < C::VCH; ++i) {
       const int ch = lane + 64 * i;
       const int slot = ch / (D / 8), dch = ch - slot * (D / 8);
+      kr[i] = __builtin_nontemporal_load((const u32x4_t*)(kp + kv_row_offset(phys, slot, kvh, p.Hkv, D) + dch * 8));
       vr[i] = __builtin_nontemporal_load((const u32x4_t*)(vp + kv_row_offset(phys, slot, kvh, p.Hkv, D) + dch * 8));
     }
   };
 
   // consume one page whose K and V are already in registers
-  auto consume = [&](int pg, const u32x4_t (&kr)[C::KS], const u32x4_t (&vr)[C::VCH]) {
+  auto consume = [&](int pg, const u32x4_t (&kr)[C::VCH], const u32x4_t (&vr)[C::VCH]) {
     const int valid = min(PAGE, L - pg * PAGE);  // slots of this page that hold tokens
     const int lo_slot = lo_t - pg * PAGE, sink_slot = p.n_sink - pg * PAGE;
     auto visible = [&](int slot) { return slot < valid && (slot >= lo_slot || slot < sink_slot); };
-    // stage V (zeros in slots that are not visible)
+    // stage K as it is and V with zeros in slots that are not visible
 #pragma unroll
     for (int i = 0; i < C::VCH; ++i) {
       const int ch = lane + 64 * i;
       const int slot = ch / (D / 8), dch = ch - slot * (D / 8);
+      *(u32x4_t*)(kst + slot * C::VROW + dch * 16) = kr[i];
       const u32x4_t val = visible(slot) ? vr[i] : u32x4_t{0u, 0u, 0u, 0u};
       *(u32x4_t*)(vst + slot * C::VROW + dch * 16) = val;
     }
+    __builtin_amdgcn_wave_barrier();
 
-    // S^T = K q^T : lane holds slots rg*4 + e for head j
+    // S^T = K q^T : lane holds slots rg*4 + e for head j; K operand: slot j,
+    // dims s*32 + rg*8 .. +7
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) sacc = mfma_16x16x32(kr[s], qreg[s], sacc);
+    for (int s = 0; s < C::KS; ++s)
+      sacc = mfma_16x16x32(*(const u32x4_t*)(kst + j * C::VROW + s * 64 + rg * 16), qreg[s], sacc);
 
     float sv[4];
     float mx = kNegInf;
@@ -249,7 +260,7 @@ __global__ __launch_bounds__(NWU * 64, ATTN_DECODE_WAVES_PER_SIMD) void decode_s
   // indexed at run time.
   int vi = v_begin;
 #if ATTN_DECODE_PREFETCH == 1
-  u32x4_t ka[C::KS], va[C::VCH], kb[C::KS], vb[C::VCH];
+  u32x4_t ka[C::VCH], va[C::VCH], kb[C::VCH], vb[C::VCH];
   if (vi < v_end) load_page(page_of(vi), ka, va);
   while (vi < v_end) {
     if (vi + 1 < v_end) load_page(page_of(vi + 1), kb, vb);
@@ -260,7 +271,7 @@ __global__ __launch_bounds__(NWU * 64, ATTN_DECODE_WAVES_PER_SIMD) void decode_s
     ++vi;
   }
 #else
-  u32x4_t ka[C::KS], va[C::VCH], kb[C::KS], vb[C::VCH], kc[C::KS], vc[C::VCH];
+  u32x4_t ka[C::VCH], va[C::VCH], kb[C::VCH], vb[C::VCH], kc[C::VCH], vc[C::VCH];
   if (vi < v_end) load_page(page_of(vi), ka, va);
   if (vi + 1 < v_end) load_page(page_of(vi + 1), kb, vb);
   while (vi < v_end) {
