@@ -40,9 +40,11 @@
 //  * K and V are read with non-temporal loads: every cached byte is read once
 //    per call, so it should not displace what other kernels keep in the
 //    caches (measured: 330 -> 313 us for the long-context decode).
-//  * Each wave keeps ATTN_DECODE_PREFETCH pages of loads in flight ahead of
-//    the page it consumes, and caches its next 64 block-table entries in one
-//    register (lane t holds entry t), so no load waits on a table lookup.
+//  * Each wave issues the loads of the next ATTN_DECODE_PREFETCH pages before
+//    it consumes the current one, and caches its next 64 block-table entries
+//    in one register (lane t holds entry t), so no load waits on a table
+//    lookup. (As compiled, the waits for the current page also take most of
+//    the next page's loads; builds that keep them in flight measured slower.)
 //  * Every wave writes its own partial; the split boundaries depend only on
 //    logical page numbers, so the result is independent of where the pages
 //    sit in the pool.
@@ -255,8 +257,8 @@ __global__ __launch_bounds__(NWU * 64, ATTN_DECODE_WAVES_PER_SIMD) void decode_s
     __builtin_amdgcn_wave_barrier();
   };
 
-  // Walk the split's pages with ATTN_DECODE_PREFETCH pages of loads in
-  // flight; the register buffers rotate by unrolling, so they are never
+  // Walk the split's pages, the next ATTN_DECODE_PREFETCH pages' loads issued
+  // ahead; the register buffers rotate by unrolling, so they are never
   // indexed at run time.
   int vi = v_begin;
 #if ATTN_DECODE_PREFETCH == 1
