@@ -32,6 +32,13 @@ and the batched decode (B=64, Hq=32, Hkv=8, d=128, 8192 tokens each) in
 GB/s, each with its roofline fraction.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+
+The default warm-up is 60 untimed steps (about 50 ms of work): under
+sustained MFMA load the part's power management needs about 30 ms to settle
+(in a kernel trace of this loop the prefill runs 570-580 us for the first two
+launches, 660-710 us for the next few and then falls steadily to 520-523 us
+after about 30 ms, while the decode stays at 281-298 us throughout), so a
+short warm-up times the transient rather than the steady state.
 """
 from __future__ import annotations
 
@@ -514,7 +521,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-chunked", action="store_true",
                     help="skip the chunked-prefill (KV append + paged prefill) and variant reports")
