@@ -141,11 +141,17 @@ def cpu_baseline(x2, x5, batches: int):
     }
 
 
-def time_calls(fn, stream, warmup: int, steps: int) -> float:
-    """Average microseconds per call from HIP events on ``stream``."""
+def time_calls(fn, stream, warmup: int, steps: int, settle_ms: float = 40.0) -> float:
+    """Average microseconds per call from HIP events on ``stream``, after at
+    least ``warmup`` untimed calls and at least ``settle_ms`` of them (the
+    clocks settle over the first tens of milliseconds of sustained load)."""
     import torch
-    for _ in range(warmup):
+    n, t0 = 0, time.perf_counter()
+    while n < warmup or (time.perf_counter() - t0) * 1e3 < settle_ms:
         fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     a.record(stream)
