@@ -33,12 +33,14 @@ GB/s, each with its roofline fraction.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 
-The default warm-up is 60 untimed steps (about 50 ms of work): under
-sustained MFMA load the part's power management needs about 30 ms to settle
-(in a kernel trace of this loop the prefill runs 570-580 us for the first two
-launches, 660-710 us for the next few and then falls steadily to 520-523 us
-after about 30 ms, while the decode stays at 281-298 us throughout), so a
-short warm-up times the transient rather than the steady state.
+Before the W warm-up steps the step runs untimed for --settle-ms (default
+50 ms; reported in the JSON line as "settle"): under sustained MFMA load the
+part's power management needs about 30 ms to settle (in a kernel trace of
+this loop after 5 warm-up steps the prefill ran 570-580 us for the first two
+launches, 660-710 us for the next few and then fell steadily to 520-523 us
+after about 30 ms, while the decode stayed at 281-298 us throughout), so
+without it a short warm-up times that transient rather than the steady
+state. Every other timed call follows at least 40 ms of untimed calls.
 """
 from __future__ import annotations
 
@@ -527,7 +529,9 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=50.0,
+                    help="untimed steps for this long before the warm-up steps (clocks settle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-chunked", action="store_true",
                     help="skip the chunked-prefill (KV append + paged prefill) and variant reports")
@@ -586,7 +590,15 @@ def main() -> int:
         if evs is not None:
             evs[2].record(stream)
 
-    log(f"warmup {args.warmup} ...")
+    n_settle, t_settle = 0, time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        step()
+        n_settle += 1
+        if n_settle % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
+    log(f"settle {n_settle} untimed steps ({settle_ms:.0f} ms), warmup {args.warmup} ...")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -623,6 +635,8 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"untimed_steps": n_settle, "ms": round(settle_ms, 1),
+                   "why": "steps run untimed before the warm-up until the clocks settle under sustained load"},
         "ms_per_step": round(total_ms / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
