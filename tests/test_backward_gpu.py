@@ -121,3 +121,30 @@ def test_workload_3_shape_full_head_group(hkv):
     dout = wl.output_gradient(x, seed=145)
     log(f"case: {x.name}, head group (b=6, kv head {hkv - 1})")
     group_check(x, dout, 6, hkv - 1)
+
+
+def test_backward_on_a_stream_other_than_the_current_one():
+    """With no workspace passed, the binding allocates the backward's scratch
+    on the launch stream, so later allocations on that stream are ordered
+    behind the kernels. The backward runs on a side stream, which at once
+    allocates and fills NaN blocks of the workspace's size; the gradients
+    must still match the oracle."""
+    x = wl.prefill_inputs(1, 300, 8, 2, 128, seed=840)
+    dout = wl.output_gradient(x, seed=841)
+    q, k, v, do = x.q.cuda(), x.k.cuda(), x.v.cuda(), dout.cuda()
+    lse = torch.empty((x.B, x.Hq, x.N), dtype=torch.float32, device="cuda")
+    o = bd.attn_prefill_ex(q, k, v, causal=True, scale=x.scale, lse=lse)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    log("case: backward B=1 N=300 Hq=8 Hkv=2 d=128 on a side stream")
+    dq, dk, dv = bd.attn_backward(q, k, v, o, do, lse, causal=True, scale=x.scale, stream=side)
+    need = bd.attn_backward_workspace_size(x.B, x.N, x.Hq)
+    with torch.cuda.stream(side):
+        junk = [torch.full((need // 4 + 4,), float("nan"), device="cuda") for _ in range(4)]
+    torch.cuda.synchronize()
+    del junk
+    rq, rk, rv = ao.sdpa_backward_ref(ao.to_bhnd(x.q, "BNHD"), ao.to_bhnd(x.k, "BNHD"), ao.to_bhnd(x.v, "BNHD"),
+                                      ao.to_bhnd(dout, "BNHD"), x.scale, True)
+    check("dq", dq.cpu(), ao.from_bhnd(rq, "BNHD"))
+    check("dk", dk.cpu(), ao.from_bhnd(rk, "BNHD"))
+    check("dv", dv.cpu(), ao.from_bhnd(rv, "BNHD"))

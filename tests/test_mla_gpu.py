@@ -84,3 +84,27 @@ def test_workload_7_full_size():
     e = np.abs(got.double().numpy() - ref)
     log(f"  whole output: max-abs {e.max():.3e} mean-abs {e.mean():.3e}")
     assert e.max() <= BF16_MAX and e.mean() <= BF16_MEAN
+
+
+def test_mla_on_a_stream_other_than_the_current_one():
+    """The MLA call's own scratch (split partials) belongs to the launch
+    stream: the decode runs on a side stream with no workspace passed, and
+    the side stream at once allocates and fills NaN blocks of the
+    workspace's size; the output must still match the oracle."""
+    x = wl.mla_decode_inputs(3, 128, 512, 64, [3000, 17, 1200], seed=960)
+    q, kv, bt, sl = x.q.cuda(), x.kv_pages.cuda(), x.block_table.cuda(), x.seq_lens.cuda()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        o = torch.empty((x.B, x.Hq, 512), dtype=torch.bfloat16, device="cuda")
+    log("case: MLA B=3 Hq=128 lens=[3000, 17, 1200] splits=5 on a side stream")
+    bd.attn_decode_mla(q, kv, bt, sl, o, scale=x.scale, num_splits=5, stream=side)
+    need = bd.attn_decode_mla_workspace_size(x.B, x.Hq, x.block_table.shape[1], 5)
+    with torch.cuda.stream(side):
+        junk = [torch.full((need // 4 + 4,), float("nan"), device="cuda") for _ in range(4)]
+    torch.cuda.synchronize()
+    del junk
+    ref = ao.mla_decode_ref(x.q, x.kv_pages, x.block_table, x.seq_lens, x.scale, 512)
+    e = np.abs(o.cpu().double().numpy() - ref)
+    log(f"  max-abs {e.max():.3e} mean-abs {e.mean():.3e}")
+    assert e.max() <= BF16_MAX and e.mean() <= BF16_MEAN
